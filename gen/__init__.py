@@ -1,0 +1,91 @@
+"""Seeded synthetic Q/K/V for dynamic block-sparse attention.
+
+The one module that both the GPU path's tests/bench and the CPU oracle's tests draw
+inputs from. It holds none of the method's arithmetic: it only draws random numbers and
+rounds them to bf16.
+
+Workloads follow the pages' video-DiT shapes (480p and 720p latents, and the ~120K-token
+sequence at which self-attention exceeds 80 % of a DiT pass, per the knowledge card
+"600倍加速，720p视频实时生成！单卡也能带的动14B模型", section 事件概述/研究问题). No dataset
+is involved; these tensors stand in for a real model's activations.
+
+Recipe (stated as a reading, since the pages give no activation statistics):
+  G1  token s <-> grid point (t, h, w) in row-major order over (T, Hg, Wg);
+  G2  phi(s) = [sin 2pi t/T, cos 2pi t/T, sin 2pi h/Hg, cos 2pi h/Hg, sin 2pi w/Wg,
+      cos 2pi w/Wg];
+  G3  one seeded matrix M in R^{6 x D} with N(0, 1/3) entries, shared by Q, K, V and all
+      heads, so each smooth entry has unit variance and Q/K block means agree where the
+      (t, h, w) phases agree -- the spatial locality that makes block selection useful;
+  G4  X = N(0,1) noise (independent per tensor) + alpha * phi(s) M, rounded to bf16
+      (round to nearest even). The tiny configuration is pure noise.
+Draw order: numpy default_rng(seed) draws M (when a grid is given), then the Q, K and V
+noise, each in C order of [B, H, S, D].
+"""
+import numpy as np
+
+CONFIGS = {
+    # Tiny dense-checkable case: 16 blocks of 64, keep 4.
+    "tiny": dict(B=1, H=2, S=1024, D=64, block=64, keep_ratio=0.25, grid=None, alpha=0.0, seed=1),
+    # 480p latent 21x30x52, keep 20 %.
+    "480p": dict(B=1, H=40, S=32760, D=128, block=128, keep_ratio=0.20, grid=(21, 30, 52),
+                 alpha=0.5, seed=2),
+    # 720p latent 21x45x80, keep 15 %.
+    "720p": dict(B=1, H=40, S=75600, D=128, block=128, keep_ratio=0.15, grid=(21, 45, 80),
+                 alpha=0.5, seed=3),
+    # ~120K-token sequence 30x64x64, keep 10 %, locality term scaled 1.0.
+    "long": dict(B=1, H=40, S=122880, D=128, block=128, keep_ratio=0.10, grid=(30, 64, 64),
+                 alpha=1.0, seed=4),
+    # FP8-QK variant on the 720p tensors (same seed); Q and K quantised per 128-token block.
+    "fp8": dict(B=1, H=40, S=75600, D=128, block=128, keep_ratio=0.15, grid=(21, 45, 80),
+                alpha=0.5, seed=3, fp8=True),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def smooth_features(grid, S: int) -> np.ndarray:
+    """phi(s) for s in [0, S): [S, 6] float64 (G1, G2)."""
+    T, Hg, Wg = grid
+    if T * Hg * Wg != S:
+        raise ValueError("grid %r does not have %d points" % (grid, S))
+    s = np.arange(S)
+    t, h, w = s // (Hg * Wg), (s // Wg) % Hg, s % Wg
+    cols = []
+    for c, period in ((t, T), (h, Hg), (w, Wg)):
+        a = 2.0 * np.pi * c / period
+        cols += [np.sin(a), np.cos(a)]
+    return np.stack(cols, axis=1)
+
+
+def make_qkv(B: int, H: int, S: int, D: int, seed: int, grid=None, alpha: float = 0.0):
+    """Seeded bf16 Q, K, V as uint16 bit arrays of shape [B, H, S, D]."""
+    rng = np.random.default_rng(seed)
+    smooth = None
+    if grid is not None:
+        M = rng.normal(0.0, np.sqrt(1.0 / 3.0), size=(6, D))
+        smooth = (alpha * (smooth_features(grid, S) @ M)).astype(np.float32)  # [S, D]
+    out = []
+    for _ in range(3):
+        x = rng.standard_normal(size=(B, H, S, D), dtype=np.float32)
+        if smooth is not None:
+            x += smooth[None, None]
+        out.append(f32_to_bf16_bits(x))
+        del x
+    return tuple(out)
+
+
+def make_config(name: str):
+    """(q, k, v, cfg) for one of CONFIGS."""
+    cfg = dict(CONFIGS[name])
+    q, k, v = make_qkv(cfg["B"], cfg["H"], cfg["S"], cfg["D"], cfg["seed"], cfg["grid"], cfg["alpha"])
+    return q, k, v, cfg

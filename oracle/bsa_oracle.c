@@ -1,0 +1,280 @@
+/*
+ * CPU oracle for dynamic block-sparse self-attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, plain, fp64 definition that the
+ * GPU library is checked against. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load it. The GPU library does not include, link or
+ * call anything here, and nothing here comes from the GPU library.
+ *
+ * What the method computes, per the pages:
+ *   [KC] "知识卡片：600倍加速，720p视频实时生成！单卡也能带的动14B模型"
+ *        (ai.cheesepanini.fun knowledge card), section 方法/产品要点, item
+ *        动态稀疏量化注意力: Query/Key block means give a quick estimate of which
+ *        attention blocks matter; at run time only the activated key blocks are
+ *        computed; typical sparsity 80-90 % (about 10-20 % of blocks kept); the
+ *        sparse path is combined with SageAttention2 into an FP8 path.
+ *   [AO] "单卡 RTX 5090 跑 Wan2.2-A14B：720p 视频生成只要 3.8 秒" (aoyii.com),
+ *        section 四步拆解, step 3 动态稀疏注意力: the same, and inside the selected
+ *        blocks the computation stays dense.
+ *
+ * Readings taken where the pages are silent (each listed in the design notes):
+ *   - block score = dot product of the two block means scaled by 1/sqrt(D);
+ *   - a fixed count k = min(n, max(1, ceil(r*n - 1e-6))) of key blocks per query
+ *     block, per (batch, head); ties go to the lower block index;
+ *   - the last block may be partial: its mean divides by its valid token count, and
+ *     its missing keys do not exist (they are never zero-padded);
+ *   - dropped blocks contribute nothing; the softmax renormalises over kept keys;
+ *     softmax scale 1/sqrt(D), no causal mask;
+ *   - a query block with an empty kept list produces a zero output row;
+ *   - FP8 is OCP E4M3FN with round-to-nearest-even, one fp32 scale = absmax/448 per
+ *     (batch, head, token block) for Q and for K separately (scale 1 when absmax=0).
+ *
+ * Layouts: tensors are [B, H, S, D] row-major; bf16 values are passed as their raw
+ * 16-bit patterns. Block i of a sequence is tokens [i*block, min(S,(i+1)*block)).
+ * All arithmetic is fp64 (bf16 and E4M3 values widen exactly).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- element access --------------------------------------------------------------- */
+
+/* bf16 is the top half of an IEEE binary32 pattern; widening is exact. */
+static double bf16_value(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP 8-bit floating point, E4M3FN: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 is subnormal (m/8 * 2^-6); no infinities; S.1111.111 is NaN;
+ * the largest finite magnitude is S.1111.110 = 448. */
+double oracle_e4m3_value(uint8_t code) {
+    int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) mag = ldexp((double)m / 8.0, -6);
+    else mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* Nearest E4M3FN code to x, ties to the even code (even mantissa), magnitudes above 448
+ * go to 448. The 127 non-negative finite codes increase with their value, so a binary
+ * search over the code values finds the two neighbours of |x|. */
+uint8_t oracle_e4m3_encode(double x) {
+    uint8_t sign = (x < 0.0 || (x == 0.0 && signbit(x))) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (isnan(x)) return 0x7F;
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    int lo = 0, hi = 0x7E;               /* value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (oracle_e4m3_value((uint8_t)mid) <= a) lo = mid; else hi = mid;
+    }
+    double dlo = a - oracle_e4m3_value((uint8_t)lo), dhi = oracle_e4m3_value((uint8_t)hi) - a;
+    int pick;
+    if (dlo < dhi) pick = lo;
+    else if (dhi < dlo) pick = hi;
+    else pick = (lo % 2 == 0) ? lo : hi;  /* tie: even mantissa */
+    return (uint8_t)(sign | pick);
+}
+
+/* A tensor as the attention definition reads it: either bf16 bits, or E4M3 codes with
+ * one scale per (batch*head, block). */
+typedef struct {
+    const uint16_t* bf16;
+    const uint8_t* e4m3;
+    const float* scale;
+    int64_t S, D, block, nblk;
+} tensor_t;
+
+static double load(const tensor_t* T, int64_t bh, int64_t t, int64_t d) {
+    int64_t off = (bh * T->S + t) * T->D + d;
+    if (T->bf16) return bf16_value(T->bf16[off]);
+    return oracle_e4m3_value(T->e4m3[off]) * (double)T->scale[bh * T->nblk + t / T->block];
+}
+
+/* ---- block partition and the k rule ----------------------------------------------- */
+
+int32_t oracle_num_blocks(int32_t S, int32_t block) {
+    if (S < 1 || block < 1) return 0;
+    return (int32_t)(((int64_t)S + block - 1) / block);
+}
+
+/* Kept key blocks per query block: the pages keep about 10-20 % of blocks; the count is
+ * the ratio times the block count, rounded up (with a 1e-6 guard against binary
+ * representation error), clamped to [1, n]. Returns 0 for invalid input. */
+int32_t oracle_num_kept(int32_t n, double keep_ratio) {
+    if (n < 1 || !(keep_ratio > 0.0) || keep_ratio > 1.0) return 0;
+    double k = ceil(keep_ratio * (double)n - 1e-6);
+    if (k < 1.0) k = 1.0;
+    if (k > (double)n) k = (double)n;
+    return (int32_t)k;
+}
+
+/* ---- step 1: block means of Q or K ([KC] 动态稀疏量化注意力: "块级均值") ------------ */
+
+void oracle_pool(const uint16_t* x, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                 double* xbar /* [B*H, n, D] */) {
+    int64_t n = oracle_num_blocks(S, block), rows = (int64_t)B * H * n;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t bh = r / n, i = r % n;
+        int64_t t0 = i * block, t1 = t0 + block < S ? t0 + block : S;
+        for (int64_t d = 0; d < D; ++d) {
+            double sum = 0.0;
+            for (int64_t t = t0; t < t1; ++t) sum += bf16_value(x[(bh * S + t) * D + d]);
+            xbar[r * D + d] = sum / (double)(t1 - t0);
+        }
+    }
+}
+
+/* ---- step 2: block-pair importance from the means ---------------------------------- */
+
+void oracle_scores(const double* qbar, const double* kbar, int32_t BH, int32_t n, int32_t D,
+                   double* s /* [BH, n, n] */) {
+    double inv = 1.0 / sqrt((double)D);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < (int64_t)BH * n; ++r) {
+        int64_t bh = r / n;
+        for (int64_t j = 0; j < n; ++j) {
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += qbar[r * D + d] * kbar[(bh * n + j) * D + d];
+            s[r * n + j] = dot * inv;
+        }
+    }
+}
+
+/* ---- step 3: keep the k most important key blocks of every query block ------------ */
+
+typedef struct { double s; int32_t j; } cand_t;
+
+/* Order: higher score first; equal scores, lower block index first. */
+static int by_score_then_index(const void* a, const void* b) {
+    const cand_t* x = (const cand_t*)a;
+    const cand_t* y = (const cand_t*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+static int by_int(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+/* col_idx[row*k .. row*k+k) = the kept blocks of row, ascending. gap[row] = k-th largest
+ * score minus (k+1)-th largest (+inf when k = n). */
+void oracle_select(const double* s, int32_t rows, int32_t n, int32_t k, int32_t* col_idx,
+                   double* gap) {
+#pragma omp parallel
+    {
+        cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)n);
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; ++r) {
+            for (int32_t j = 0; j < n; ++j) { c[j].s = s[r * n + j]; c[j].j = j; }
+            qsort(c, (size_t)n, sizeof(cand_t), by_score_then_index);
+            for (int32_t m = 0; m < k; ++m) col_idx[r * k + m] = c[m].j;
+            qsort(col_idx + r * k, (size_t)k, sizeof(int32_t), by_int);
+            if (gap) gap[r] = (k < n) ? c[k - 1].s - c[k].s : INFINITY;
+        }
+        free(c);
+    }
+}
+
+/* ---- step 4: attention over the kept blocks only ----------------------------------- */
+
+/* For every requested query token, softmax(Q_t K_u^T / sqrt(D)) V_u over the keys u of
+ * the kept blocks of t's block ([AO] 动态稀疏注意力: dense inside the selected blocks).
+ * tokens[m] = bh*S + t; NULL means all B*H*S tokens in order. out is [ntok, D]. */
+static void attention_core(const tensor_t* Q, const tensor_t* K, const tensor_t* V, int64_t BH,
+                           const int32_t* row_ptr, const int32_t* col_idx,
+                           const int64_t* tokens, int64_t ntok, double* out) {
+    int64_t S = Q->S, D = Q->D, block = Q->block, n = Q->nblk;
+    double inv = 1.0 / sqrt((double)D);
+    (void)BH;
+#pragma omp parallel
+    {
+        double* logit = (double*)malloc(sizeof(double) * (size_t)S);
+        int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)S);
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t m = 0; m < ntok; ++m) {
+            int64_t flat = tokens ? tokens[m] : m;
+            int64_t bh = flat / S, t = flat % S, row = bh * n + t / block;
+            double* o = out + m * D;
+            int64_t nk = 0;
+            for (int32_t p = row_ptr[row]; p < row_ptr[row + 1]; ++p) {
+                int64_t j = col_idx[p], u0 = j * block, u1 = u0 + block < S ? u0 + block : S;
+                for (int64_t u = u0; u < u1; ++u) key[nk++] = u;
+            }
+            for (int64_t d = 0; d < D; ++d) { qrow[d] = load(Q, bh, t, d); o[d] = 0.0; }
+            if (nk == 0) continue;
+            double mx = -INFINITY;
+            for (int64_t a = 0; a < nk; ++a) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d) dot += qrow[d] * load(K, bh, key[a], d);
+                logit[a] = dot * inv;
+                if (logit[a] > mx) mx = logit[a];
+            }
+            double denom = 0.0;
+            for (int64_t a = 0; a < nk; ++a) { logit[a] = exp(logit[a] - mx); denom += logit[a]; }
+            for (int64_t a = 0; a < nk; ++a) {
+                double p = logit[a] / denom;
+                for (int64_t d = 0; d < D; ++d) o[d] += p * load(V, bh, key[a], d);
+            }
+        }
+        free(logit); free(key); free(qrow);
+    }
+}
+
+void oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t B,
+                      int32_t H, int32_t S, int32_t D, int32_t block, const int32_t* row_ptr,
+                      const int32_t* col_idx, const int64_t* tokens, int64_t ntok, double* out) {
+    int64_t n = oracle_num_blocks(S, block);
+    tensor_t Q = {q, NULL, NULL, S, D, block, n}, K = {k, NULL, NULL, S, D, block, n},
+             V = {v, NULL, NULL, S, D, block, n};
+    if (!tokens) ntok = (int64_t)B * H * S;
+    attention_core(&Q, &K, &V, (int64_t)B * H, row_ptr, col_idx, tokens, ntok, out);
+}
+
+/* ---- FP8 path ([KC] 动态稀疏量化注意力: SageAttention2 FP8 sparse path) ------------ */
+
+/* Per (batch*head, block): scale = absmax/448 in fp32 (1 when the block is all zero);
+ * code = nearest E4M3FN to x/scale, the division done in IEEE fp32. */
+void oracle_quantize_fp8(const uint16_t* x, int32_t B, int32_t H, int32_t S, int32_t D,
+                         int32_t block, uint8_t* codes, float* scale /* [B*H, n] */) {
+    int64_t n = oracle_num_blocks(S, block), rows = (int64_t)B * H * n;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t bh = r / n, i = r % n;
+        int64_t t0 = i * block, t1 = t0 + block < S ? t0 + block : S;
+        float amax = 0.0f;
+        for (int64_t off = (bh * S + t0) * D; off < (bh * S + t1) * D; ++off) {
+            float a = fabsf((float)bf16_value(x[off]));
+            if (a > amax) amax = a;
+        }
+        float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+        scale[r] = sc;
+        for (int64_t off = (bh * S + t0) * D; off < (bh * S + t1) * D; ++off) {
+            float y = (float)bf16_value(x[off]) / sc;
+            codes[off] = oracle_e4m3_encode((double)y);
+        }
+    }
+}
+
+/* Attention with Q and K given as E4M3 codes and per-block scales, V as bf16 (the
+ * quantised path; a diagnostic that separates quantisation error from kernel error). */
+void oracle_attention_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                          const float* k_scale, const uint16_t* v, int32_t B, int32_t H,
+                          int32_t S, int32_t D, int32_t block, const int32_t* row_ptr,
+                          const int32_t* col_idx, const int64_t* tokens, int64_t ntok,
+                          double* out) {
+    int64_t n = oracle_num_blocks(S, block);
+    tensor_t Q = {NULL, q8, q_scale, S, D, block, n}, K = {NULL, k8, k_scale, S, D, block, n},
+             V = {v, NULL, NULL, S, D, block, n};
+    if (!tokens) ntok = (int64_t)B * H * S;
+    attention_core(&Q, &K, &V, (int64_t)B * H, row_ptr, col_idx, tokens, ntok, out);
+}

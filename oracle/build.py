@@ -1,0 +1,24 @@
+"""Compile the CPU oracle (plain C, fp64, OpenMP) into oracle/libbsa_oracle.so.
+
+Test infrastructure only: see oracle/__init__.py.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "bsa_oracle.c")
+LIB = os.path.join(HERE, "libbsa_oracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-Wall", "-Wextra", "-shared", "-fPIC",
+           SRC, "-o", LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,39 @@
+"""The seeded input generator: determinism, shapes, bf16 rounding, locality structure."""
+import numpy as np
+import torch
+
+import gen
+
+
+def test_same_seed_same_bytes():
+    a = gen.make_qkv(1, 2, 300, 16, 7, grid=(3, 10, 10), alpha=0.5)
+    b = gen.make_qkv(1, 2, 300, 16, 7, grid=(3, 10, 10), alpha=0.5)
+    for x, y in zip(a, b):
+        assert x.dtype == np.uint16 and x.shape == (1, 2, 300, 16)
+        assert np.array_equal(x, y)
+    c = gen.make_qkv(1, 2, 300, 16, 8, grid=(3, 10, 10), alpha=0.5)
+    assert not np.array_equal(a[0], c[0])
+
+
+def test_bf16_rounding_matches_torch():
+    x = np.random.default_rng(0).normal(0, 3, 100000).astype(np.float32)
+    x = np.concatenate([x, np.float32([1.00390625, 1.01171875, -2.00390625, 0.0, -0.0])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(gen.f32_to_bf16_bits(x), ref)
+    assert np.array_equal(gen.bf16_bits_to_f32(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_config_shapes():
+    for name, c in gen.CONFIGS.items():
+        if c["grid"] is not None:
+            T, Hg, Wg = c["grid"]
+            assert T * Hg * Wg == c["S"], name
+    assert gen.CONFIGS["tiny"]["grid"] is None
+
+
+def test_smooth_term_has_unit_scale_and_period():
+    phi = gen.smooth_features((4, 5, 6), 120)
+    assert phi.shape == (120, 6)
+    np.testing.assert_allclose(np.sum(phi ** 2, axis=1), 3.0, atol=1e-12)
+    # one period per axis: token (t=0,h=0,w=0) equals the wrap-around point
+    np.testing.assert_allclose(phi[0], gen.smooth_features((4, 5, 6), 120)[0])
