@@ -1,0 +1,241 @@
+"""Benchmark: dynamic block-sparse attention on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input that is
+already resident in HBM: bsa_select (block means, block scores, top-k) followed by
+bsa_forward (attention over the kept blocks), both through the C ABI. The workload is the
+720p-shaped video-DiT attention: B=1, H=40, S=75600 (21x45x80 latent), D=128, block 128,
+keep_ratio 0.15 (89 of 591 key blocks per query block).
+
+Prints one JSON line. `value` is milliseconds per step (lower is better). The line also
+carries the attention kernel's own time, its kept-block TFLOP/s against the bf16 MFMA
+peak (`roofline`), the fp8-QK variant, a dense (keep_ratio 1) forward for context, and
+the CPU oracle timed on a bounded sample on this host (`cpu_baseline`).
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_bsa_amd", "csrc", "attention.hip")
+
+
+def kept_flops(row_ptr, col_idx, S, block):
+    """4 * D-free part: sum over rows of (valid queries) x (valid keys in kept blocks).
+    Multiply by 4*D for QK^T and PV multiply-adds (2 flops each)."""
+    n = (S + block - 1) // block
+    sizes = np.full(n, block, dtype=np.int64)
+    sizes[-1] = S - (n - 1) * block
+    rp = row_ptr.astype(np.int64)
+    keys = np.add.reduceat(sizes[col_idx.astype(np.int64)], rp[:-1]) if col_idx.size else np.zeros(rp.size - 1)
+    keys = np.where(np.diff(rp) > 0, keys, 0)
+    qsz = np.tile(sizes, (rp.size - 1) // n)
+    return int(np.sum(qsz * keys))
+
+
+def traffic_from_profile(kernel_sha):
+    """HBM bytes per attention launch from the committed PMC summary, if it was taken on
+    the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, "attn_bf16_720p_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b) or m_sha.group(1) != kernel_sha:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(q, k, v, cfg, budget_tokens):
+    """Time the CPU oracle on this host: full selection, attention on a token sample,
+    scaled to one whole call."""
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    B, H, S, D = q.shape
+    t0 = time.perf_counter()
+    ref = oracle.select(q, k, cfg["block"], cfg["keep_ratio"])
+    t_sel = time.perf_counter() - t0
+    tok = np.random.default_rng(0).choice(B * H * S, size=budget_tokens, replace=False)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, cfg["block"], ref["row_ptr"], ref["col_idx"], tokens=tok)
+    t_att = time.perf_counter() - t0
+    total_s = t_sel + t_att * (B * H * S) / budget_tokens
+    return {
+        "value": round(total_s * 1e3, 1), "unit": "ms/step", "cores": int(os.environ["OMP_NUM_THREADS"]),
+        "kind": "oracle",
+        "sample": "full selection (%.2f s) + attention for %d of %d query rows (%.2f s), scaled to all rows"
+                  % (t_sel, budget_tokens, B * H * S, t_att),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="720p", choices=["480p", "720p", "long"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=8192, help="query rows the CPU oracle computes")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (PMC calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the design notes "
+              "describe how the work would shard by head).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dynamic_block_sparse_bsa_amd as bsa
+    import gen
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    q, k, v, cfg = gen.make_config(args.config)
+    B, H, S, D = q.shape
+    block, r = cfg["block"], cfg["keep_ratio"]
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    n = bsa.bsa_num_blocks(S, block)
+    kept = bsa.bsa_num_kept(n, r)
+    rows = B * H * n
+    ws = torch.empty(bsa.bsa_select_workspace_bytes(B, H, S, D, block), dtype=torch.uint8, device=dev)
+    rp = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(rows * kept, dtype=torch.int32, device=dev)
+    out = torch.empty_like(qd)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        bsa.bsa_select(qd, kd, block, r, workspace=ws, row_ptr=rp, col_idx=ci)
+        if ev is not None:
+            ev[1].record()
+        bsa.bsa_forward(qd, kd, vd, block, rp, ci, out=out)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    step_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in events]))
+
+    flop = 4.0 * D * kept_flops(rp.cpu().numpy(), ci.cpu().numpy(), S, block)
+    fwd_tflops = flop / (fwd_ms * 1e-3) / 1e12
+    kernel_sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    pool_bytes = 2 * B * H * S * D * 2
+
+    # fp8-QK variant: quantise Q and K, then attention with fp8 QK^T.
+    q8, qs = bsa.bsa_quantize_fp8(qd, block)
+    k8, ks = bsa.bsa_quantize_fp8(kd, block)
+    out8 = torch.empty_like(qd)
+    for _ in range(2):
+        bsa.bsa_forward_fp8(q8, qs, k8, ks, vd, block, rp, ci, out=out8)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    reps = max(3, args.steps // 2)
+    e[0].record()
+    for _ in range(reps):
+        bsa.bsa_quantize_fp8(qd, block, codes=q8, scale=qs)
+        bsa.bsa_quantize_fp8(kd, block, codes=k8, scale=ks)
+    e[1].record()
+    for _ in range(reps):
+        bsa.bsa_forward_fp8(q8, qs, k8, ks, vd, block, rp, ci, out=out8)
+    e[2].record()
+    torch.cuda.synchronize()
+    quant_ms = e[0].elapsed_time(e[1]) / reps
+    fwd8_ms = e[1].elapsed_time(e[2]) / reps
+
+    dense = None
+    if not args.no_dense:
+        rp1 = torch.arange(rows + 1, dtype=torch.int32, device=dev) * n
+        ci1 = torch.arange(n, dtype=torch.int32, device=dev).repeat(rows)
+        bsa.bsa_forward(qd, kd, vd, block, rp1, ci1, out=out)
+        torch.cuda.synchronize()
+        e2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e2[0].record()
+        for _ in range(2):
+            bsa.bsa_forward(qd, kd, vd, block, rp1, ci1, out=out)
+        e2[1].record()
+        torch.cuda.synchronize()
+        dms = e2[0].elapsed_time(e2[1]) / 2
+        dflop = 4.0 * D * (B * H) * S * S
+        dense = {"forward_ms": round(dms, 3), "tflops": round(dflop / dms / 1e9, 1),
+                 "frac_bf16_peak": round(dflop / dms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        del rp1, ci1
+
+    if args.calib_copy_mib:
+        x = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, k, v, cfg, args.cpu_sample)
+
+    result = {
+        "metric": "ms/attention call + kept-block TFLOP/s (% MFMA peak), 720p-shaped S=75600",
+        "value": round(step_ms, 4),
+        "unit": "ms/step (bsa_select + bsa_forward)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded noise + smooth (t,h,w) locality term, bf16)",
+        "config": {"workload": "%s: B=%d H=%d S=%d D=%d block=%d keep_ratio=%g (%d of %d key blocks kept)"
+                               % (args.config, B, H, S, D, block, r, kept, n),
+                   "global_batch": B, "seq_len": S, "heads": H, "head_dim": D, "block": block,
+                   "keep_ratio": r, "parallelism": "single GPU"},
+        "attention_ms": round(fwd_ms, 4),
+        "select_ms": round(sel_ms, 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "kept_tflop_per_call": round(flop / 1e12, 4),
+        "kept_tflops": round(fwd_tflops, 1),
+        "kept_tflops_per_step": round(flop / (step_ms * 1e-3) / 1e12, 1),
+        "frac_bf16_mfma_peak": round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
+        "select_hbm_gbs": round(pool_bytes / (sel_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_from_profile(kernel_sha),
+                     "kernel": "attn_kernel<128,128,bf16>"},
+        "fp8_qk": {"quantize_ms": round(quant_ms, 4), "attention_ms": round(fwd8_ms, 4),
+                   "kept_tflops": round(flop / (fwd8_ms * 1e-3) / 1e12, 1),
+                   "frac_mixed_peak": round(flop / (fwd8_ms * 1e-3) / 1e12 / (2 / (1 / FP8_PEAK_TFLOPS + 1 / BF16_PEAK_TFLOPS)), 4)},
+        "dense_keep_ratio_1": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+"""Dynamic block-sparse self-attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over libbsa.so, the C-ABI library declared in include/bsa.h. This
+module only marshals arguments: torch provides device memory and the current stream,
+and every step of the computation runs in libbsa's HIP kernels. There is no CPU or
+PyTorch fallback: if libbsa.so is missing or a call fails, an exception is raised.
+
+Function names match the C entry points. Tensors are contiguous [B, H, S, D] on a HIP
+device: bf16 for q, k, v and outputs, uint8 (E4M3FN bit patterns) for fp8 codes.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BsaError", "lib_path", "bsa_num_blocks", "bsa_num_kept", "bsa_select_workspace_bytes",
+    "bsa_pool", "bsa_select", "bsa_forward", "bsa_quantize_fp8", "bsa_forward_fp8",
+    "bsa_check_csr", "bsa_status_string", "bsa_last_error",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libbsa.so")
+
+BSA_OK = 0
+STATUS_NAMES = {0: "BSA_OK", 1: "BSA_ERR_INVALID_ARGUMENT", 2: "BSA_ERR_UNSUPPORTED",
+                3: "BSA_ERR_WORKSPACE_TOO_SMALL", 4: "BSA_ERR_NO_DEVICE", 5: "BSA_ERR_HIP"}
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, str(status)), message))
+        self.status = status
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError("libbsa.so is not built (expected at %s); run __graft_entry__.build()" % lib_path)
+    lib = ctypes.CDLL(lib_path)
+    P, i32, f64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
+    sig = {
+        "bsa_num_blocks": (i32, [i32, i32]),
+        "bsa_num_kept": (i32, [i32, f64]),
+        "bsa_select_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "bsa_pool": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P]),
+        "bsa_select": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, f64, P, P, P, sz, P]),
+        "bsa_forward": (ctypes.c_int, [P, P, P, i32, i32, i32, i32, i32, P, P, P, P]),
+        "bsa_quantize_fp8": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P]),
+        "bsa_forward_fp8": (ctypes.c_int, [P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]),
+        "bsa_check_csr": (ctypes.c_int, [P, P, i32, i32]),
+        "bsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "bsa_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != BSA_OK:
+        raise BsaError(status, _load().bsa_last_error().decode())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev_tensor(t, name, dtypes, ndim=4):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a HIP device (got %s)" % (name, t.device))
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions" % (name, ndim))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+_ONE_BYTE = (torch.uint8, torch.int8, torch.float8_e4m3fn)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def bsa_num_blocks(S: int, block: int) -> int:
+    return _load().bsa_num_blocks(S, block)
+
+
+def bsa_num_kept(n_blocks: int, keep_ratio: float) -> int:
+    return _load().bsa_num_kept(n_blocks, keep_ratio)
+
+
+def bsa_select_workspace_bytes(B, H, S, D, block) -> int:
+    return _load().bsa_select_workspace_bytes(B, H, S, D, block)
+
+
+def bsa_pool(x, block: int, out=None):
+    """fp32 block means [B, H, n, D] of a bf16 [B, H, S, D] tensor."""
+    _dev_tensor(x, "x", (torch.bfloat16,))
+    B, H, S, D = x.shape
+    n = bsa_num_blocks(S, block)
+    if out is None:
+        out = torch.empty((B, H, n, D), dtype=torch.float32, device=x.device)
+    _check(_load().bsa_pool(_p(x), B, H, S, D, block, _p(out), _stream(x)))
+    return out
+
+
+def bsa_select(q, k, block: int, keep_ratio: float, workspace=None, row_ptr=None, col_idx=None):
+    """Kept key-block lists (row_ptr int32 [B*H*n+1], col_idx int32 [B*H*n*kept])."""
+    _dev_tensor(q, "q", (torch.bfloat16,))
+    _dev_tensor(k, "k", (torch.bfloat16,))
+    if q.shape != k.shape:
+        raise ValueError("q and k shapes differ")
+    B, H, S, D = q.shape
+    n = bsa_num_blocks(S, block)
+    kept = bsa_num_kept(n, keep_ratio)
+    if kept == 0:
+        raise BsaError(1, "keep_ratio must be in (0, 1] (got %r)" % (keep_ratio,))
+    rows = B * H * n
+    ws_bytes = bsa_select_workspace_bytes(B, H, S, D, block)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
+    if col_idx is None:
+        col_idx = torch.empty(rows * kept, dtype=torch.int32, device=q.device)
+    _check(_load().bsa_select(_p(q), _p(k), B, H, S, D, block, keep_ratio, _p(row_ptr), _p(col_idx),
+                              _p(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
+    return row_ptr, col_idx
+
+
+def _csr(row_ptr, col_idx, device):
+    for t, name in ((row_ptr, "row_ptr"), (col_idx, "col_idx")):
+        _dev_tensor(t, name, (torch.int32,), ndim=1)
+        if t.device != device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def bsa_forward(q, k, v, block: int, row_ptr, col_idx, out=None):
+    """Attention over the kept blocks; bf16 [B, H, S, D]."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_tensor(t, name, (torch.bfloat16,))
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v shapes differ")
+    _csr(row_ptr, col_idx, q.device)
+    B, H, S, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor(out, "out", (torch.bfloat16,))
+    _check(_load().bsa_forward(_p(q), _p(k), _p(v), B, H, S, D, block, _p(row_ptr), _p(col_idx), _p(out),
+                               _stream(q)))
+    return out
+
+
+def bsa_quantize_fp8(x, block: int, codes=None, scale=None):
+    """(codes uint8 [B,H,S,D] holding E4M3FN, scale fp32 [B,H,n]) per token block."""
+    _dev_tensor(x, "x", (torch.bfloat16,))
+    B, H, S, D = x.shape
+    n = bsa_num_blocks(S, block)
+    if codes is None:
+        codes = torch.empty((B, H, S, D), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((B, H, n), dtype=torch.float32, device=x.device)
+    _check(_load().bsa_quantize_fp8(_p(x), B, H, S, D, block, _p(codes), _p(scale), _stream(x)))
+    return codes, scale
+
+
+def bsa_forward_fp8(q8, q_scale, k8, k_scale, v, block: int, row_ptr, col_idx, out=None):
+    """Attention with E4M3FN Q/K codes and per-block scales, bf16 V; bf16 output."""
+    _dev_tensor(q8, "q_e4m3", _ONE_BYTE)
+    _dev_tensor(k8, "k_e4m3", _ONE_BYTE)
+    _dev_tensor(v, "v", (torch.bfloat16,))
+    if not (q8.shape == k8.shape == v.shape):
+        raise ValueError("q_e4m3, k_e4m3 and v shapes differ")
+    B, H, S, D = v.shape
+    n = bsa_num_blocks(S, block)
+    for t, name in ((q_scale, "q_scale"), (k_scale, "k_scale")):
+        _dev_tensor(t, name, (torch.float32,), ndim=None)
+        if t.numel() != B * H * n:
+            raise ValueError("%s must have B*H*n = %d entries" % (name, B * H * n))
+    _csr(row_ptr, col_idx, v.device)
+    if out is None:
+        out = torch.empty_like(v)
+    _dev_tensor(out, "out", (torch.bfloat16,))
+    _check(_load().bsa_forward_fp8(_p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(v), B, H, S, D, block,
+                                   _p(row_ptr), _p(col_idx), _p(out), _stream(v)))
+    return out
+
+
+def bsa_check_csr(row_ptr, col_idx, rows: int, n_blocks: int):
+    """Validate a host-side CSR (numpy or CPU tensors); raises BsaError on a violation."""
+    import numpy as np
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    if rp.size != rows + 1:
+        raise BsaError(1, "row_ptr must have rows + 1 entries")
+    if rp[-1] > ci.size:
+        raise BsaError(1, "col_idx shorter than row_ptr[rows]")
+    _check(_load().bsa_check_csr(ctypes.c_void_p(rp.ctypes.data), ctypes.c_void_p(ci.ctypes.data), rows, n_blocks))
+
+
+def bsa_status_string(status: int) -> str:
+    return _load().bsa_status_string(status).decode()
+
+
+def bsa_last_error() -> str:
+    return _load().bsa_last_error().decode()

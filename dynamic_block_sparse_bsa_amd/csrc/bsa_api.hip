@@ -1,0 +1,226 @@
+// C ABI of libbsa (declared in include/bsa.h): argument checks, device checks, launches.
+//
+// Every entry point checks its arguments on the host first and returns before touching
+// HIP when they are bad, so the error paths work on machines without a GPU. No C++
+// exception crosses the interface.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/bsa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bsa_status fail(bsa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape rules shared by every compute call.
+bsa_status check_shape(int32_t B, int32_t H, int32_t S, int32_t D, int32_t block) {
+    if (B < 1 || H < 1 || S < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "B, H and S must be >= 1 (got %d, %d, %d)", B, H, S);
+    if (D != 64 && D != 128) return fail(BSA_ERR_UNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+    if (block != 64 && block != 128) return fail(BSA_ERR_UNSUPPORTED, "block must be 64 or 128 (got %d)", block);
+    const int64_t elems = (int64_t)B * H * S * D;
+    if (elems >= ((int64_t)1 << 40)) return fail(BSA_ERR_UNSUPPORTED, "tensor too large");
+    const int64_t rows = (int64_t)B * H * ((S + block - 1) / block);
+    if (rows >= ((int64_t)1 << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many block rows");
+    return BSA_OK;
+}
+
+// Per-device check: a gfx950 device is current. Cached per device id.
+struct DevInfo {
+    bool known = false;
+    bool ok = false;
+};
+std::mutex g_dev_mu;
+std::vector<DevInfo> g_dev;
+
+bsa_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(BSA_ERR_NO_DEVICE, "no HIP device is available");
+    }
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+    DevInfo& di = g_dev[dev];
+    if (!di.known) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(BSA_ERR_HIP, "hipGetDeviceProperties failed for device %d", dev);
+        }
+        di.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        di.known = true;
+        if (!di.ok) return fail(BSA_ERR_UNSUPPORTED, "device %d is %s; libbsa is built for gfx950 only", dev, prop.gcnArchName);
+    }
+    if (!di.ok) return fail(BSA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return BSA_OK;
+}
+
+bsa_status hip_result(hipError_t e, const char* what) {
+    if (e == hipSuccess) return BSA_OK;
+    return fail(BSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr double kLog2e = 1.4426950408889634;
+
+}  // namespace
+
+extern "C" {
+
+int32_t bsa_num_blocks(int32_t S, int32_t block) {
+    if (S < 1 || block < 1) return 0;
+    return (int32_t)(((int64_t)S + block - 1) / block);
+}
+
+int32_t bsa_num_kept(int32_t n_blocks, double keep_ratio) {
+    if (n_blocks < 1 || !(keep_ratio > 0.0) || keep_ratio > 1.0) return 0;
+    double k = ceil(keep_ratio * (double)n_blocks - 1e-6);
+    if (k < 1.0) k = 1.0;
+    if (k > (double)n_blocks) k = (double)n_blocks;
+    return (int32_t)k;
+}
+
+size_t bsa_select_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t block) {
+    if (B < 1 || H < 1 || S < 1 || D < 1 || block < 1) return 0;
+    const size_t n = (size_t)bsa_num_blocks(S, block);
+    return round_up(2 * (size_t)B * H * n * D * sizeof(float), 256);
+}
+
+bsa_status bsa_pool(const void* x, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block, float* xbar,
+                    void* hip_stream) {
+    bsa_status st = check_shape(B, H, S, D, block);
+    if (st != BSA_OK) return st;
+    if (!x || !xbar) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(x) || !aligned16(xbar)) return fail(BSA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    if ((st = check_device()) != BSA_OK) return st;
+    return hip_result(bsa::launch_pool(x, B * H, S, D, block, xbar, false, as_stream(hip_stream)), "pool launch");
+}
+
+bsa_status bsa_select(const void* q, const void* k, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                      double keep_ratio, int32_t* row_ptr, int32_t* col_idx, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+    bsa_status st = check_shape(B, H, S, D, block);
+    if (st != BSA_OK) return st;
+    if (!q || !k || !row_ptr || !col_idx || !workspace) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(workspace))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "q, k and workspace must be 16-byte aligned");
+    if (((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u)) return fail(BSA_ERR_INVALID_ARGUMENT, "misaligned CSR arrays");
+    const int32_t n = bsa_num_blocks(S, block);
+    const int32_t kept = bsa_num_kept(n, keep_ratio);
+    if (kept == 0) return fail(BSA_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1] (got %g)", keep_ratio);
+    if (n > bsa::kMaxSelectBlocks) return fail(BSA_ERR_UNSUPPORTED, "bsa_select supports at most %d blocks per sequence (got %d)", bsa::kMaxSelectBlocks, n);
+    if ((int64_t)B * H * n * kept >= ((int64_t)1 << 31)) return fail(BSA_ERR_UNSUPPORTED, "kept-block list too long for int32 indices");
+    const size_t need = bsa_select_workspace_bytes(B, H, S, D, block);
+    if (workspace_bytes < need) return fail(BSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    if ((st = check_device()) != BSA_OK) return st;
+    float* qbar = (float*)workspace;
+    float* kbarT = qbar + (size_t)B * H * n * D;
+    hipStream_t s = as_stream(hip_stream);
+    if ((st = hip_result(bsa::launch_pool_qk(q, k, B * H, S, D, block, qbar, kbarT, s), "pool launch")) != BSA_OK) return st;
+    return hip_result(bsa::launch_select(qbar, kbarT, B * H, n, D, kept, row_ptr, col_idx, s), "select launch");
+}
+
+static bsa_status forward_common(const void* q, const float* q_scale, const void* k, const float* k_scale, const void* v,
+                                 int32_t B, int32_t H, int32_t S, int32_t D, int32_t block, const int32_t* row_ptr,
+                                 const int32_t* col_idx, void* out, void* hip_stream, bool fp8) {
+    bsa_status st = check_shape(B, H, S, D, block);
+    if (st != BSA_OK) return st;
+    if (!q || !k || !v || !row_ptr || !col_idx || !out) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (fp8 && (!q_scale || !k_scale)) return fail(BSA_ERR_INVALID_ARGUMENT, "null scale pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+    if (((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u)) return fail(BSA_ERR_INVALID_ARGUMENT, "misaligned CSR arrays");
+    if (out == q || out == k || out == v) return fail(BSA_ERR_INVALID_ARGUMENT, "out must not alias an input");
+    if ((st = check_device()) != BSA_OK) return st;
+    bsa::AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.out = out;
+    a.BH = B * H;
+    a.S = S;
+    a.n = bsa_num_blocks(S, block);
+    a.sm_scale_log2 = (float)(kLog2e / sqrt((double)D));
+    return hip_result(bsa::launch_attention(a, D, block, fp8, as_stream(hip_stream)), "attention launch");
+}
+
+bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t B, int32_t H, int32_t S, int32_t D,
+                       int32_t block, const int32_t* row_ptr, const int32_t* col_idx, void* out, void* hip_stream) {
+    return forward_common(q, nullptr, k, nullptr, v, B, H, S, D, block, row_ptr, col_idx, out, hip_stream, false);
+}
+
+bsa_status bsa_forward_fp8(const void* q_e4m3, const float* q_scale, const void* k_e4m3, const float* k_scale,
+                           const void* v, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* out, void* hip_stream) {
+    return forward_common(q_e4m3, q_scale, k_e4m3, k_scale, v, B, H, S, D, block, row_ptr, col_idx, out, hip_stream,
+                          true);
+}
+
+bsa_status bsa_quantize_fp8(const void* x, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block, void* x_e4m3,
+                            float* scale, void* hip_stream) {
+    bsa_status st = check_shape(B, H, S, D, block);
+    if (st != BSA_OK) return st;
+    if (!x || !x_e4m3 || !scale) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(x) || !aligned16(x_e4m3) || ((uintptr_t)scale & 3u))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "x and x_e4m3 must be 16-byte aligned");
+    if ((st = check_device()) != BSA_OK) return st;
+    return hip_result(bsa::launch_quantize_fp8(x, B * H, S, D, block, x_e4m3, scale, as_stream(hip_stream)),
+                      "quantize launch");
+}
+
+bsa_status bsa_check_csr(const int32_t* row_ptr, const int32_t* col_idx, int32_t rows, int32_t n_blocks) {
+    if (!row_ptr || rows < 0 || n_blocks < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "bad arguments");
+    if (row_ptr[0] != 0) return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr[0] = %d, expected 0", row_ptr[0]);
+    for (int32_t r = 0; r < rows; ++r) {
+        const int32_t a = row_ptr[r], b = row_ptr[r + 1];
+        if (b < a) return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr decreases at row %d", r);
+        if (b > a && !col_idx) return fail(BSA_ERR_INVALID_ARGUMENT, "null col_idx");
+        for (int32_t p = a; p < b; ++p) {
+            const int32_t j = col_idx[p];
+            if (j < 0 || j >= n_blocks) return fail(BSA_ERR_INVALID_ARGUMENT, "row %d: index %d outside [0, %d)", r, j, n_blocks);
+            if (p > a && j <= col_idx[p - 1]) return fail(BSA_ERR_INVALID_ARGUMENT, "row %d: indices not strictly ascending", r);
+        }
+    }
+    return BSA_OK;
+}
+
+const char* bsa_status_string(bsa_status status) {
+    switch (status) {
+        case BSA_OK: return "BSA_OK";
+        case BSA_ERR_INVALID_ARGUMENT: return "BSA_ERR_INVALID_ARGUMENT";
+        case BSA_ERR_UNSUPPORTED: return "BSA_ERR_UNSUPPORTED";
+        case BSA_ERR_WORKSPACE_TOO_SMALL: return "BSA_ERR_WORKSPACE_TOO_SMALL";
+        case BSA_ERR_NO_DEVICE: return "BSA_ERR_NO_DEVICE";
+        case BSA_ERR_HIP: return "BSA_ERR_HIP";
+    }
+    return "BSA_ERR_UNKNOWN";
+}
+
+const char* bsa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Internal launcher interface between the C ABI (bsa_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+struct AttnArgs {
+    const void* q;          // bf16 or E4M3 [B,H,S,D]
+    const void* k;          // bf16 or E4M3 [B,H,S,D]
+    const void* v;          // bf16 [B,H,S,D]
+    const float* q_scale;   // [B*H*n] (fp8 only)
+    const float* k_scale;   // [B*H*n] (fp8 only)
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    void* out;              // bf16 [B,H,S,D]
+    int BH, S, n;
+    float sm_scale_log2;    // log2(e) / sqrt(D)
+};
+
+hipError_t launch_attention(const AttnArgs& a, int D, int block, bool fp8, hipStream_t stream);
+
+// Block means of x (bf16 [BH,S,D]) into fp32: row-major [BH,n,D], or [BH,D,n] if transposed.
+hipError_t launch_pool(const void* x, int BH, int S, int D, int block, float* xbar, bool transposed,
+                       hipStream_t stream);
+
+// Two pooled tensors in one launch: qbar row-major, kbar transposed.
+hipError_t launch_pool_qk(const void* q, const void* k, int BH, int S, int D, int block, float* qbar,
+                          float* kbarT, hipStream_t stream);
+
+// Scores from pooled means and top-k per row; writes row_ptr (uniform) and col_idx.
+hipError_t launch_select(const float* qbar, const float* kbarT, int BH, int n, int D, int kept,
+                         int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
+
+hipError_t launch_quantize_fp8(const void* x, int BH, int S, int D, int block, void* codes, float* scale,
+                               hipStream_t stream);
+
+constexpr int kSelectRowsPerGroup = 4;
+constexpr int kMaxSelectBlocks = 8192;
+
+}  // namespace bsa

@@ -1,0 +1,251 @@
+// Block pooling, block-pair scoring and top-k selection, and the FP8 quantiser, for gfx950.
+//
+// Method: the knowledge card "600倍加速，720p视频实时生成！单卡也能带的动14B模型", section
+// 方法/产品要点, item 动态稀疏量化注意力: Query/Key block means give a quick estimate of
+// attention importance; about 10-20 % of the key blocks are kept per query block; the
+// sparse path becomes an FP8 path (SageAttention2). The aoyii.com article "单卡 RTX 5090
+// 跑 Wan2.2-A14B", section 四步拆解, step 3 动态稀疏注意力, says the same.
+//
+// Pooling and quantisation are HBM-bound streaming kernels: one workgroup per (b*h, token
+// block) reads the block once with coalesced 16-byte loads. Scoring reads the pooled
+// means (a few MB); selection is an exact radix select per row on 32-bit order-preserving
+// keys with ties broken towards the lower block index.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace bsa {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---- pooling -------------------------------------------------------------------------
+// Thread t handles 16-byte chunk (t % CH) of the row, for tokens t / CH, t / CH + TL, ...
+template <int D>
+__global__ void __launch_bounds__(kThreads) pool_kernel(const uint16_t* __restrict__ x0, const uint16_t* __restrict__ x1,
+                                                        int BH, int S, int block, int n, float* __restrict__ out0,
+                                                        float* __restrict__ out1, int transposed_mask) {
+    constexpr int CH = D / 8, TL = kThreads / CH;
+    __shared__ float red[TL][D + 4];
+    const int which = blockIdx.y;
+    const uint16_t* x = which ? x1 : x0;
+    float* out = which ? out1 : out0;
+    const bool transposed = (transposed_mask >> which) & 1;
+    const int rowi = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = rowi / n, i = rowi - bh * n;
+    const int t0 = i * block;
+    const int cnt = (S - t0) < block ? (S - t0) : block;
+    const int c = threadIdx.x % CH, tl = threadIdx.x / CH;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const uint16_t* base = x + ((int64_t)bh * S + t0) * D + 8 * c;
+    for (int t = tl; t < cnt; t += TL) {
+        u32x4 w = *(const u32x4*)(base + (int64_t)t * D);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += __uint_as_float(w[e] << 16);
+            acc[2 * e + 1] += __uint_as_float(w[e] & 0xFFFF0000u);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[tl][8 * c + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        float s = 0.0f;
+        for (int r = 0; r < TL; ++r) s += red[r][d];
+        const float mean = s / (float)cnt;
+        if (transposed) out[((int64_t)bh * D + d) * n + i] = mean;
+        else out[((int64_t)bh * n + i) * D + d] = mean;
+    }
+}
+
+// ---- scores + top-k ------------------------------------------------------------------
+// One workgroup per (b*h, group of R query blocks); wave w selects for query block w of
+// the group. Scores live in LDS (R * n floats).
+template <int D>
+__global__ void __launch_bounds__(kThreads) select_kernel(const float* __restrict__ qbar, const float* __restrict__ kbarT,
+                                                          int BH, int n, int kept, float scale,
+                                                          int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
+    constexpr int R = kSelectRowsPerGroup;
+    extern __shared__ float smem[];
+    float* qs = smem;            // [R][D]
+    float* sc = smem + R * D;    // [R][n]
+    const int groups = (n + R - 1) / R;
+    const int gi = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = gi / groups, i0 = (gi - bh * groups) * R;
+
+    for (int e = threadIdx.x; e < R * D; e += kThreads) {
+        const int r = e / D, d = e - r * D;
+        qs[e] = (i0 + r < n) ? qbar[((int64_t)bh * n + i0 + r) * D + d] : 0.0f;
+    }
+    __syncthreads();
+
+    const float* kb = kbarT + (int64_t)bh * D * n;
+    for (int j = threadIdx.x; j < n; j += kThreads) {
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+        for (int d = 0; d < D; ++d) {
+            const float kv = kb[(int64_t)d * n + j];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(qs[r * D + d], kv, acc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) sc[r * n + j] = acc[r] * scale;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i = i0 + w;
+    if (w >= R || i >= n) return;
+    uint32_t* key = (uint32_t*)(sc + w * n);
+    for (int j = lane; j < n; j += 64) key[j] = ordered_key(sc[w * n + j]);
+    // (each lane rewrites only the entries it reads below; a wave sees its own writes)
+
+    // Largest T with #(key >= T) >= kept: the kept-th largest key.
+    uint32_t T = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        int cnt = 0;
+        for (int j0 = 0; j0 < n; j0 += 64) {
+            const int j = j0 + lane;
+            const bool ge = (j < n) && key[j] >= cand;
+            cnt += __popcll(__ballot(ge));
+        }
+        if (cnt >= kept) T = cand;
+    }
+    int gt = 0;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        const int j = j0 + lane;
+        gt += __popcll(__ballot((j < n) && key[j] > T));
+    }
+    const int need = kept - gt;  // how many blocks with key == T to take, lowest index first
+    const int64_t row = (int64_t)bh * n + i;
+    int32_t* out = col_idx + row * kept;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int pos = 0, ties = 0;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        const int j = j0 + lane;
+        const uint32_t kj = (j < n) ? key[j] : 0u;
+        const bool eq = (j < n) && kj == T;
+        const uint64_t eqm = __ballot(eq);
+        const int tie_rank = ties + __popcll(eqm & below);
+        const bool sel = (j < n) && (kj > T || (eq && tie_rank < need));
+        const uint64_t selm = __ballot(sel);
+        if (sel) out[pos + __popcll(selm & below)] = j;
+        pos += __popcll(selm);
+        ties += __popcll(eqm);
+    }
+    if (lane == 0) {
+        row_ptr[row] = (int32_t)(row * kept);
+        if (row == (int64_t)BH * n - 1) row_ptr[row + 1] = (int32_t)((row + 1) * kept);
+    }
+}
+
+// ---- FP8 quantisation ------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(kThreads) quant_kernel(const uint16_t* __restrict__ x, int BH, int S, int block, int n,
+                                                         uint8_t* __restrict__ codes, float* __restrict__ scale) {
+    constexpr int CH = D / 8;
+    __shared__ float wmax[kThreads / 64];
+    const int rowi = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = rowi / n, i = rowi - bh * n;
+    const int t0 = i * block;
+    const int cnt = (S - t0) < block ? (S - t0) : block;
+    const int64_t base = ((int64_t)bh * S + t0) * D;
+    const int chunks = cnt * CH;
+    float amax = 0.0f;
+    for (int q = threadIdx.x; q < chunks; q += kThreads) {
+        u32x4 w = *(const u32x4*)(x + base + 8 * (int64_t)q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[e] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[e] & 0xFFFF0000u)));
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    if (threadIdx.x == 0) scale[rowi] = sc;
+    for (int q = threadIdx.x; q < chunks; q += kThreads) {
+        u32x4 w = *(const u32x4*)(x + base + 8 * (int64_t)q);
+        u32x2 packed;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            int v = 0;
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w[2 * e] << 16) / sc,
+                                                __uint_as_float(w[2 * e] & 0xFFFF0000u) / sc, v, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w[2 * e + 1] << 16) / sc,
+                                                __uint_as_float(w[2 * e + 1] & 0xFFFF0000u) / sc, v, true);
+            packed[e] = (uint32_t)v;
+        }
+        *(u32x2*)(codes + base + 8 * (int64_t)q) = packed;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const void* x, int BH, int S, int D, int block, float* xbar, bool transposed, hipStream_t stream) {
+    const int n = (S + block - 1) / block;
+    dim3 grid(BH * n, 1);
+    if (D == 128)
+        hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x, (const uint16_t*)x, BH, S,
+                           block, n, xbar, xbar, transposed ? 3 : 0);
+    else
+        hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(kThreads), 0, stream, (const uint16_t*)x, (const uint16_t*)x, BH, S,
+                           block, n, xbar, xbar, transposed ? 3 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_qk(const void* q, const void* k, int BH, int S, int D, int block, float* qbar, float* kbarT,
+                          hipStream_t stream) {
+    const int n = (S + block - 1) / block;
+    dim3 grid(BH * n, 2);
+    if (D == 128)
+        hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kThreads), 0, stream, (const uint16_t*)q, (const uint16_t*)k, BH, S,
+                           block, n, qbar, kbarT, 2);
+    else
+        hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(kThreads), 0, stream, (const uint16_t*)q, (const uint16_t*)k, BH, S,
+                           block, n, qbar, kbarT, 2);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const float* qbar, const float* kbarT, int BH, int n, int D, int kept, int32_t* row_ptr,
+                         int32_t* col_idx, hipStream_t stream) {
+    constexpr int R = kSelectRowsPerGroup;
+    const int groups = (n + R - 1) / R;
+    const size_t smem = sizeof(float) * (size_t)R * (D + n);
+    const float scale = 1.0f / sqrtf((float)D);
+    const void* fn = D == 128 ? (const void*)select_kernel<128> : (const void*)select_kernel<64>;
+    if (smem > 65536) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+    }
+    if (D == 128)
+        hipLaunchKernelGGL(select_kernel<128>, dim3(BH * groups), dim3(kThreads), smem, stream, qbar, kbarT, BH, n, kept,
+                           scale, row_ptr, col_idx);
+    else
+        hipLaunchKernelGGL(select_kernel<64>, dim3(BH * groups), dim3(kThreads), smem, stream, qbar, kbarT, BH, n, kept,
+                           scale, row_ptr, col_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const void* x, int BH, int S, int D, int block, void* codes, float* scale,
+                               hipStream_t stream) {
+    const int n = (S + block - 1) / block;
+    if (D == 128)
+        hipLaunchKernelGGL(quant_kernel<128>, dim3(BH * n), dim3(kThreads), 0, stream, (const uint16_t*)x, BH, S, block, n,
+                           (uint8_t*)codes, scale);
+    else
+        hipLaunchKernelGGL(quant_kernel<64>, dim3(BH * n), dim3(kThreads), 0, stream, (const uint16_t*)x, BH, S, block, n,
+                           (uint8_t*)codes, scale);
+    return hipGetLastError();
+}
+
+}  // namespace bsa

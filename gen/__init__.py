@@ -18,9 +18,14 @@ Recipe (stated as a reading, since the pages give no activation statistics):
       (t, h, w) phases agree -- the spatial locality that makes block selection useful;
   G4  X = N(0,1) noise (independent per tensor) + alpha * phi(s) M, rounded to bf16
       (round to nearest even). The tiny configuration is pure noise.
-Draw order: numpy default_rng(seed) draws M (when a grid is given), then the Q, K and V
-noise, each in C order of [B, H, S, D].
+Streams: numpy SeedSequence(seed) spawns 1 + 3*B*H child seeds; child 0 draws M (when a
+grid is given), child 1 + t*B*H + (b*H + h) draws the [S, D] noise of tensor t (Q, K, V in
+that order) for batch b, head h. The streams are independent of how many threads fill
+them, so the bytes depend on the seed only.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 CONFIGS = {
@@ -44,9 +49,14 @@ CONFIGS = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    u = x.reshape(-1).view(np.uint32)
+    out = np.empty(u.size, dtype=np.uint16)
+    step = 1 << 24
+    for a in range(0, u.size, step):  # chunked: full-size tensors hold ~10^9 values
+        c = u[a:a + step]
+        # finite inputs cannot overflow 32 bits here (largest is 0xFF7FFFFF + 0x8000)
+        out[a:a + step] = ((c + np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -69,18 +79,23 @@ def smooth_features(grid, S: int) -> np.ndarray:
 
 def make_qkv(B: int, H: int, S: int, D: int, seed: int, grid=None, alpha: float = 0.0):
     """Seeded bf16 Q, K, V as uint16 bit arrays of shape [B, H, S, D]."""
-    rng = np.random.default_rng(seed)
+    children = np.random.SeedSequence(seed).spawn(1 + 3 * B * H)
     smooth = None
     if grid is not None:
-        M = rng.normal(0.0, np.sqrt(1.0 / 3.0), size=(6, D))
+        M = np.random.default_rng(children[0]).normal(0.0, np.sqrt(1.0 / 3.0), size=(6, D))
         smooth = (alpha * (smooth_features(grid, S) @ M)).astype(np.float32)  # [S, D]
-    out = []
-    for _ in range(3):
-        x = rng.standard_normal(size=(B, H, S, D), dtype=np.float32)
+    out = [np.empty((B, H, S, D), dtype=np.uint16) for _ in range(3)]
+
+    def fill(job):
+        t, bh = divmod(job, B * H)
+        x = np.random.default_rng(children[1 + job]).standard_normal(size=(S, D), dtype=np.float32)
         if smooth is not None:
-            x += smooth[None, None]
-        out.append(f32_to_bf16_bits(x))
-        del x
+            x += smooth
+        out[t][bh // H, bh % H] = f32_to_bf16_bits(x)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fill, range(3 * B * H)))
     return tuple(out)
 
 

@@ -1,0 +1,146 @@
+/*
+ * bsa.h -- C ABI of libbsa: dynamic block-sparse self-attention on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method, as the pages describe it:
+ *   [KC] "知识卡片：600倍加速，720p视频实时生成！单卡也能带的动14B模型"
+ *        (ai.cheesepanini.fun knowledge card), section 方法/产品要点, item
+ *        动态稀疏量化注意力: the block-level means of Query and Key give a quick estimate
+ *        of which attention blocks matter; at run time only the activated key blocks
+ *        are computed; typical sparsity is 80-90 % (about 10-20 % of the blocks kept);
+ *        the sparse path is combined with SageAttention2 into an FP8 path.
+ *   [AO] "单卡 RTX 5090 跑 Wan2.2-A14B：720p 视频生成只要 3.8 秒" (aoyii.com), section
+ *        四步拆解, step 3 动态稀疏注意力: the same, and inside the selected blocks the
+ *        computation stays dense, to keep the GPU's throughput.
+ *
+ * The calls follow that split: bsa_select() estimates importance from block means and
+ * returns the kept key-block lists; bsa_forward() computes attention over only those
+ * blocks. bsa_quantize_fp8() and bsa_forward_fp8() are the FP8 path.
+ *
+ * Conventions shared by every call:
+ *   - Tensors are contiguous [B, H, S, D] row-major (D fastest); q, k, v and out hold
+ *     bf16, x_e4m3 holds OCP E4M3FN bytes. Every tensor base address is device memory
+ *     aligned to 16 bytes.
+ *   - Token block i of a sequence is tokens [i*block, min(S, (i+1)*block)); there are
+ *     n = ceil(S/block) blocks, the last possibly partial. Query and key blocks are the
+ *     same partition.
+ *   - Supported: D in {64, 128}; block in {64, 128}; S >= 1; B, H >= 1; B*H*S*D < 2^40;
+ *     n <= 8192 for bsa_select. Other shapes return BSA_ERR_UNSUPPORTED.
+ *   - Kept-block lists are CSR over the B*H*n query-block rows, row r = (b*H + h)*n + i:
+ *     row_ptr int32 [B*H*n + 1], col_idx int32 [row_ptr[B*H*n]]; each row's key-block
+ *     indices are strictly ascending in [0, n).
+ *   - Ownership: the caller allocates and frees every buffer (inputs, outputs,
+ *     workspace). The library never allocates device memory, never frees, and never
+ *     synchronises; it keeps only a per-device table of properties.
+ *   - Streams: every compute call is enqueued on hip_stream (a hipStream_t; NULL is the
+ *     null stream) and returns before the GPU finishes. Outputs must not alias inputs.
+ *   - Errors: arguments are checked on the host before any HIP call, so a bad argument
+ *     returns an error without touching the GPU and without side effects. Faults on the
+ *     device surface at the caller's next synchronisation. No C++ exception crosses this
+ *     interface. bsa_last_error() gives a thread-local message for the last failure.
+ *
+ * Thread safety: calls may come from several host threads; calls that share output
+ * buffers on overlapping streams race like any other GPU work.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsa_status {
+    BSA_OK = 0,
+    BSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misaligned, bad ratio     */
+    BSA_ERR_UNSUPPORTED = 2,        /* shape outside the supported set, or not gfx950   */
+    BSA_ERR_WORKSPACE_TOO_SMALL = 3,
+    BSA_ERR_NO_DEVICE = 4,          /* no HIP device visible                             */
+    BSA_ERR_HIP = 5                 /* a HIP runtime call failed (message in last_error) */
+} bsa_status;
+
+/* Number of token blocks, ceil(S / block); 0 when S < 1 or block < 1. Host only. */
+int32_t bsa_num_blocks(int32_t S, int32_t block);
+
+/* Kept key blocks per query block for a keep ratio r in (0, 1]: [KC] keeps about
+ * 10-20 % of the blocks; this library rounds r*n up (with a 1e-6 guard against binary
+ * representation error, evaluated in double) and clamps to [1, n]. Returns 0 for
+ * n < 1 or r outside (0, 1] (NaN included). Host only. */
+int32_t bsa_num_kept(int32_t n_blocks, double keep_ratio);
+
+/* Bytes of device workspace bsa_select needs: the fp32 block means of Q and K,
+ * 2 * B*H*n*D * 4, rounded up to 256. 0 on invalid shape. Host only. */
+size_t bsa_select_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t block);
+
+/* Block means ([KC] 动态稀疏量化注意力: "块级均值"): xbar[b,h,i,:] = the mean of x over
+ * the valid tokens of block i, accumulated in fp32. x: bf16 [B,H,S,D] (device).
+ * xbar: fp32 [B,H,n,D] (device, caller-allocated). Exposed for parity checks; bsa_select
+ * computes the same means internally. */
+bsa_status bsa_pool(const void* x, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                    float* xbar, void* hip_stream);
+
+/* Importance estimate and block selection ([KC] 动态稀疏量化注意力; [AO] 动态稀疏注意力).
+ * For every (b, h) and query block i: score s_ij = mean(Q_i) . mean(K_j) / sqrt(D) in
+ * fp32 for every key block j; keep the k = bsa_num_kept(n, keep_ratio) blocks with the
+ * highest scores (equal scores: the lower index first); write them ascending.
+ *   q, k:      bf16 [B,H,S,D] (device).
+ *   row_ptr:   int32 [B*H*n + 1] (device); written as row_ptr[r] = r*k.
+ *   col_idx:   int32 [B*H*n*k] (device).
+ *   workspace: device scratch of at least bsa_select_workspace_bytes(); contents on
+ *              return are the pooled means (undefined layout).
+ * Errors: INVALID_ARGUMENT (null/misaligned pointer, keep_ratio not in (0,1]),
+ * UNSUPPORTED, WORKSPACE_TOO_SMALL, NO_DEVICE, HIP. */
+bsa_status bsa_select(const void* q, const void* k, int32_t B, int32_t H, int32_t S, int32_t D,
+                      int32_t block, double keep_ratio, int32_t* row_ptr, int32_t* col_idx,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Sparse attention over the kept blocks ([KC] 动态稀疏量化注意力: only the activated key
+ * blocks are computed; [AO] 动态稀疏注意力: dense inside each selected block). For query
+ * token t of block i: out_t = sum_u softmax_u(q_t . k_u / sqrt(D)) v_u over the valid
+ * tokens u of the blocks listed in row (b*H+h)*n + i. No causal mask. Blocks not listed
+ * contribute nothing; a row with an empty list gives zeros. Logits, softmax and
+ * accumulation are fp32, both products run on bf16 MFMA, out is rounded to bf16.
+ *   q, k, v: bf16 [B,H,S,D] (device).   out: bf16 [B,H,S,D] (device).
+ *   row_ptr, col_idx: any CSR as described above (device), e.g. bsa_select's output.
+ *   Entries outside [0, n) are skipped; a row whose end precedes its start is empty.
+ *   The CSR arrays themselves must be as long as row_ptr says. */
+bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t B, int32_t H,
+                       int32_t S, int32_t D, int32_t block, const int32_t* row_ptr,
+                       const int32_t* col_idx, void* out, void* hip_stream);
+
+/* FP8 quantisation for the FP8 path ([KC] 动态稀疏量化注意力: SageAttention2 FP8 sparse
+ * attention). Per (b, h, token block): scale = absmax / 448 in fp32 (1 when the block is
+ * all zeros); code = x / scale (IEEE fp32 division) rounded to the nearest OCP E4M3FN
+ * value, ties to even.
+ *   x: bf16 [B,H,S,D] (device). x_e4m3: uint8 [B,H,S,D] (device). scale: fp32 [B,H,n]. */
+bsa_status bsa_quantize_fp8(const void* x, int32_t B, int32_t H, int32_t S, int32_t D,
+                            int32_t block, void* x_e4m3, float* scale, void* hip_stream);
+
+/* bsa_forward with Q and K given as E4M3FN codes plus per-block scales (from
+ * bsa_quantize_fp8, with the same block size): q.k^T runs on fp8 MFMA with fp32
+ * accumulation and the two block scales folded into the logit scale; the softmax is
+ * fp32; P and V are bf16 on bf16 MFMA; out is bf16. Same CSR rules as bsa_forward. */
+bsa_status bsa_forward_fp8(const void* q_e4m3, const float* q_scale, const void* k_e4m3,
+                           const float* k_scale, const void* v, int32_t B, int32_t H, int32_t S,
+                           int32_t D, int32_t block, const int32_t* row_ptr,
+                           const int32_t* col_idx, void* out, void* hip_stream);
+
+/* Host-side validator for a CSR held in host memory: row_ptr[0] == 0, non-decreasing,
+ * every row's indices strictly ascending in [0, n_blocks). Returns BSA_OK or
+ * BSA_ERR_INVALID_ARGUMENT with the first violation in bsa_last_error(). */
+bsa_status bsa_check_csr(const int32_t* row_ptr_host, const int32_t* col_idx_host, int32_t rows,
+                         int32_t n_blocks);
+
+/* Static name of a status code. */
+const char* bsa_status_string(bsa_status status);
+
+/* Thread-local message describing the last failed call on this thread ("" if none). */
+const char* bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

@@ -1,0 +1,93 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+Every kept-block list is compared with the oracle's (the list criterion in parity.py).
+Outputs are compared on sampled query rows, which the oracle computes one by one: a
+seeded random sample plus the first and last token of several heads (the last block is
+partial at 480p and 720p), on both the oracle's and the GPU's lists.
+"""
+import functools
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import dynamic_block_sparse_bsa_amd as bsa
+import gen
+import oracle
+from parity import BF16_MAX, BF16_MEAN, FP8_MAX, check_lists, errors, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=1)
+def workload(name):
+    q, k, v, cfg = gen.make_config(name)
+    ref = oracle.select(q, k, cfg["block"], cfg["keep_ratio"])
+    return q, k, v, cfg, ref
+
+
+def sample_tokens(B, H, S, count=256, seed=0):
+    rng = np.random.default_rng(seed)
+    edge = []
+    for bh in (0, B * H // 2, B * H - 1):
+        edge += [bh * S, bh * S + S - 1, bh * S + (S - 1) // 128 * 128]
+    return np.unique(np.concatenate([rng.integers(0, B * H * S, count), edge]))
+
+
+def rows_of(out, tok, D):
+    return to_f64(out.reshape(-1, D)[torch.from_numpy(tok).to(out.device)])
+
+
+@pytest.mark.parametrize("name", ["480p", "720p", "long"])
+def test_full_size_bf16(name):
+    q, k, v, cfg, ref = workload(name)
+    B, H, S, D, block = q.shape + (cfg["block"],)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    rp, ci = bsa.bsa_select(qd, kd, block, cfg["keep_ratio"])
+    out = bsa.bsa_forward(qd, kd, vd, block, rp, ci)
+    grp, gci = rp.cpu().numpy(), ci.cpu().numpy()
+    exact, ties = check_lists(grp, gci, ref)
+    print("%s: %d rows bit-exact, %d near-tie rows within tolerance" % (name, exact, ties))
+
+    tok = sample_tokens(B, H, S)
+    expect = oracle.attention(q, k, v, block, grp, gci, tokens=tok)
+    mx, mean = errors(rows_of(out, tok, D), expect)
+    print("%s bf16 on GPU lists: max %.3e mean %.3e over %d rows" % (name, mx, mean, tok.size))
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+    orp, oci = torch.from_numpy(ref["row_ptr"]).cuda(), torch.from_numpy(ref["col_idx"]).cuda()
+    out2 = bsa.bsa_forward(qd, kd, vd, block, orp, oci)
+    expect2 = oracle.attention(q, k, v, block, ref["row_ptr"], ref["col_idx"], tokens=tok)
+    mx, mean = errors(rows_of(out2, tok, D), expect2)
+    print("%s bf16 on oracle lists: max %.3e mean %.3e" % (name, mx, mean))
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+    del qd, kd, vd, out, out2
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_full_size_fp8():
+    q, k, v, cfg, ref = workload("fp8")
+    B, H, S, D, block = q.shape + (cfg["block"],)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    q8, qs = bsa.bsa_quantize_fp8(qd, block)
+    k8, ks = bsa.bsa_quantize_fp8(kd, block)
+    oq8, oqs = oracle.quantize_fp8(q, block)
+    ok8, oks = oracle.quantize_fp8(k, block)
+    assert np.array_equal(qs.cpu().numpy(), oqs) and np.array_equal(ks.cpu().numpy(), oks)
+    assert np.array_equal(q8.cpu().numpy(), oq8) and np.array_equal(k8.cpu().numpy(), ok8)
+    rp, ci = bsa.bsa_select(qd, kd, block, cfg["keep_ratio"])
+    check_lists(rp.cpu().numpy(), ci.cpu().numpy(), ref)
+    out = bsa.bsa_forward_fp8(q8, qs, k8, ks, vd, block, rp, ci)
+    tok = sample_tokens(B, H, S, seed=1)
+    got = rows_of(out, tok, D)
+    grp, gci = rp.cpu().numpy(), ci.cpu().numpy()
+    expect = oracle.attention(q, k, v, block, grp, gci, tokens=tok)
+    mx, mean = errors(got, expect)
+    print("fp8 vs unquantised oracle: max %.3e mean %.3e" % (mx, mean))
+    assert mx <= FP8_MAX
+    expect8 = oracle.attention_fp8(oq8, oqs, ok8, oks, v, block, grp, gci, tokens=tok)
+    mx8, mean8 = errors(got, expect8)
+    print("fp8 vs oracle on the same E4M3 operands: max %.3e mean %.3e" % (mx8, mean8))
+    assert mx8 <= BF16_MAX and mean8 <= BF16_MEAN
