@@ -42,6 +42,13 @@ namespace {
 
 constexpr int KT = 64;  // keys per sub-tile
 
+// s_waitcnt immediate for gfx9-family: vmcnt(0), expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// 2^x on the transcendental unit (one v_exp_f32). Results below 2^-126 may flush to zero,
+// which is harmless for softmax weights.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Physical 16-byte slot of chunk c in row r of an LDS tile with `chunks` chunks per row.
 template <int chunks>
 __device__ __forceinline__ int swz(int r, int c) {
@@ -77,17 +84,27 @@ struct Cfg {
     static constexpr int KCH = KROWB / 16;
     static constexpr int VTILE = KT * VROWB;
     static constexpr int KTILE = KT * KROWB;
-    static constexpr int VLOADS = VTILE / (NT * 16);   // 16-byte loads per thread per tile
-    static constexpr int KLOADS = KTILE / (NT * 16);
     static constexpr int STAGE = KTILE + VTILE;
     static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;  // MFMA k-steps of S^T
+    // Direct global->LDS loads move 1 KiB per wave instruction ("segment").
+    static constexpr int KRPS = 1024 / KROWB, VRPS = 1024 / VROWB;  // rows per segment
+    static constexpr int KSEGW = KTILE / 1024 / NW, VSEGW = VTILE / 1024 / NW;  // per wave
 };
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+// One 16-byte direct global->LDS load per lane; the wave writes the 1 KiB at lds_dst
+// (wave-uniform) with lane l's data at lds_dst + 16*l.
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)lds_dst, 16, 0, 0);
+}
 
 template <int D, int BLK, bool FP8>
 __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_kernel(const AttnArgs a) {
     using C = Cfg<D, BLK, FP8>;
-    static_assert(C::VLOADS >= 1 && C::KLOADS >= 1, "tile too small for the workgroup");
+    static_assert(C::KSEGW >= 1 && C::VSEGW >= 1, "tile too small for the workgroup");
     __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE];
 
     const int tid = threadIdx.x;
@@ -98,12 +115,14 @@ attn_kernel(const AttnArgs a) {
     const int row = xcd_remap(blockIdx.x, gridDim.x);  // (b*H + h) * n + i
     const int bh = row / n, iq = row - bh * n;
     const int64_t bh_off = (int64_t)bh * S;  // token offset of this (b, h)
+    const char* kbh = (const char*)a.k + bh_off * C::KROWB;
+    const char* vbh = (const char*)a.v + bh_off * C::VROWB;
 
     // ---- Q operand (B of S^T = K Q^T), kept in registers --------------------------------
     const int q_tok = iq * BLK + wave * 32 + l32;
     const int q_ld = q_tok < S ? q_tok : S - 1;
-    typedef typename std::conditional<FP8, i32x8, bf16x8>::type qfrag_t;
-    qfrag_t qf[C::QSTEPS];
+    typedef typename std::conditional<FP8, i32x8, bf16x8>::type frag_t;
+    frag_t qf[C::QSTEPS];
     if constexpr (FP8) {
         const uint8_t* qp = (const uint8_t*)a.q + (bh_off + q_ld) * D + 32 * h;
 #pragma unroll
@@ -117,75 +136,123 @@ attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < C::QSTEPS; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
     }
+    // Retire the Q loads here, on every path: otherwise the wait-count analysis can carry
+    // them as pending into the main loop, where an in-order vmcnt wait for them would also
+    // wait for the next sub-tile's prefetch and serialise the pipeline.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     float qscale_log2 = a.sm_scale_log2;
     if constexpr (FP8) qscale_log2 *= a.q_scale[row];
 
-    // ---- kept-block list --------------------------------------------------------------
+    // ---- kept-block list ----------------------------------------------------------------
+    // The row's list is read through a 64-entry window held one entry per lane (and, for the
+    // fp8 path, the matching key-block scales); entries are fetched with readlane, so the
+    // walk needs no memory access except one window load per 64 blocks.
     int p = a.row_ptr[row];
     int pend = a.row_ptr[row + 1];
     if (pend < p) pend = p;
+    int wbase = p, win = -1;
+    float kswin = 0.0f;
+    auto load_window = [&](int base) {
+        wbase = base;
+        const int idx = base + lane;
+        win = idx < pend ? a.col_idx[idx] : -1;
+        if constexpr (FP8) kswin = (win >= 0 && win < n) ? a.k_scale[(int64_t)bh * n + win] : 0.0f;
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    };
+    load_window(p);
+    auto entry = [&](int idx) -> int {  // col_idx[idx], idx < pend
+        if (idx - wbase >= 64) load_window(idx);
+        return __builtin_amdgcn_readlane(win, idx - wbase);
+    };
+    auto entry_kscale = [&](int idx) -> float {  // k_scale of entry idx (window is current)
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kswin), idx - wbase));
+    };
     auto valid_block = [&](int idx) -> int {  // next position >= idx holding a block in [0,n)
         while (idx < pend) {
-            int j = a.col_idx[idx];
+            int j = entry(idx);
             if (j >= 0 && j < n) return idx;
             ++idx;
         }
         return pend;
     };
-    p = valid_block(p);
-
     // Sub-tile cursor: (list position, key offset inside the block).
-    int cur_p = p, cur_k = 0;
     auto tile_keys = [&](int pp, int kk) -> int {  // valid keys in sub-tile, 0 at the end
         if (pp >= pend) return 0;
-        int j = a.col_idx[pp];
+        int j = entry(pp);
         int rem = S - (j * BLK + kk);
         int inblk = BLK - kk;
         int nk = rem < inblk ? rem : inblk;
         return nk < KT ? nk : KT;
     };
     auto advance = [&](int& pp, int& kk) {
-        int j = a.col_idx[pp];
+        int j = entry(pp);
         int next = kk + KT;
         if (next < BLK && j * BLK + next < S) { kk = next; return; }
         kk = 0;
         pp = valid_block(pp + 1);
     };
 
-    // ---- staging registers ----------------------------------------------------------
-    u32x4 kreg[C::KLOADS], vreg[C::VLOADS];
-    auto load_tile = [&](int pp, int kk) {
-        const int j = a.col_idx[pp];
-        const int key0 = j * BLK + kk;
+    // ---- direct global->LDS tile loads ------------------------------------------------
+    // Segment sg of a tile holds rows [sg*RPS, (sg+1)*RPS); lane l fills slot l % CH of row
+    // sg*RPS + l / CH, i.e. it fetches chunk (slot ^ swz(row)) of that row, so the tile
+    // lands swizzled. Wave w fills segments w, w + NW, ...
+    uint32_t k_src[C::KSEGW], v_src[C::VSEGW];
 #pragma unroll
-        for (int x = 0; x < C::KLOADS; ++x) {
-            int ci = tid + C::NT * x, r = ci / C::KCH, c = ci % C::KCH;
-            int key = key0 + r;
-            key = key < S ? key : S - 1;
-            kreg[x] = *(const u32x4*)((const char*)a.k + (bh_off + key) * C::KROWB + 16 * c);
-        }
+    for (int x = 0; x < C::KSEGW; ++x) {
+        const int r = (x * C::NW + wave) * C::KRPS + lane / C::KCH;
+        k_src[x] = r * C::KROWB + 16 * swz<C::KCH>(r, lane % C::KCH);
+    }
 #pragma unroll
-        for (int x = 0; x < C::VLOADS; ++x) {
-            int ci = tid + C::NT * x, r = ci / C::VCH, c = ci % C::VCH;
-            int key = key0 + r;
-            key = key < S ? key : S - 1;
-            vreg[x] = *(const u32x4*)((const char*)a.v + (bh_off + key) * C::VROWB + 16 * c);
+    for (int x = 0; x < C::VSEGW; ++x) {
+        const int r = (x * C::NW + wave) * C::VRPS + lane / C::VCH;
+        v_src[x] = r * C::VROWB + 16 * swz<C::VCH>(r, lane % C::VCH);
+    }
+    auto issue_tile = [&](int pp, int kk, char* stage_base) {
+        const int key0 = entry(pp) * BLK + kk;
+        const char* kb = kbh + (int64_t)key0 * C::KROWB;
+        const char* vb = vbh + (int64_t)key0 * C::VROWB;
+        if (key0 + KT <= S) {
+#pragma unroll
+            for (int x = 0; x < C::KSEGW; ++x) dma16(kb + k_src[x], stage_base + (x * C::NW + wave) * 1024);
+#pragma unroll
+            for (int x = 0; x < C::VSEGW; ++x)
+                dma16(vb + v_src[x], stage_base + C::KTILE + (x * C::NW + wave) * 1024);
+        } else {  // partial tile: rows past the end re-read the last row (masked later)
+            const int last = S - 1 - key0;
+#pragma unroll
+            for (int x = 0; x < C::KSEGW; ++x) {
+                const int r = (x * C::NW + wave) * C::KRPS + lane / C::KCH;
+                const int rr = r < last ? r : last;
+                dma16(kb + rr * C::KROWB + (k_src[x] - r * C::KROWB), stage_base + (x * C::NW + wave) * 1024);
+            }
+#pragma unroll
+            for (int x = 0; x < C::VSEGW; ++x) {
+                const int r = (x * C::NW + wave) * C::VRPS + lane / C::VCH;
+                const int rr = r < last ? r : last;
+                dma16(vb + rr * C::VROWB + (v_src[x] - r * C::VROWB),
+                      stage_base + C::KTILE + (x * C::NW + wave) * 1024);
+            }
         }
     };
-    auto store_tile = [&](int stage) {
-        char* kt = lds + stage * C::STAGE;
-        char* vt = kt + C::KTILE;
+
+    // ---- per-lane LDS read offsets (kh = 0, m = 0; other halves are constant offsets) ----
+    constexpr int KSLOTS = FP8 ? 2 * C::QSTEPS : C::QSTEPS;  // 16-byte K reads per 32 keys
+    uint32_t k_rd[KSLOTS];
 #pragma unroll
-        for (int x = 0; x < C::KLOADS; ++x) {
-            int ci = tid + C::NT * x, r = ci / C::KCH, c = ci % C::KCH;
-            *(u32x4*)(kt + r * C::KROWB + 16 * swz<C::KCH>(r, c)) = kreg[x];
-        }
+    for (int st = 0; st < KSLOTS; ++st) {
+        const int c = FP8 ? (4 * (st >> 1) + 2 * h + (st & 1)) : (2 * st + h);
+        k_rd[st] = l32 * C::KROWB + 16 * swz<C::KCH>(l32, c);
+    }
+    const int gi = lane & 15;
+    uint32_t v_rd1[D / 32], v_rd2[D / 32];
 #pragma unroll
-        for (int x = 0; x < C::VLOADS; ++x) {
-            int ci = tid + C::NT * x, r = ci / C::VCH, c = ci % C::VCH;
-            *(u32x4*)(vt + r * C::VROWB + 16 * swz<C::VCH>(r, c)) = vreg[x];
-        }
-    };
+    for (int ds = 0; ds < D / 32; ++ds) {
+        const int dcol = 32 * ds + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+        const int c = dcol >> 3, coff = (dcol & 7) * 2;
+        const int r1 = 4 * h + (gi >> 2), r2 = r1 + 8;
+        v_rd1[ds] = r1 * C::VROWB + 16 * swz<C::VCH>(r1, c) + coff;
+        v_rd2[ds] = r2 * C::VROWB + 16 * swz<C::VCH>(r2, c) + coff;
+    }
 
     // ---- accumulators and softmax state (per lane: query column l32) -------------------
     f32x16 o[D / 32];
@@ -194,45 +261,29 @@ attn_kernel(const AttnArgs a) {
     float m_used = -__builtin_inff();
     float lsum = 0.0f;
 
-    int nkeys = tile_keys(cur_p, cur_k);
-    if (nkeys > 0) {
-        load_tile(cur_p, cur_k);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    int stage = 0;
-    while (nkeys > 0) {
-        // Prefetch the next sub-tile into registers.
-        int nxt_p = cur_p, nxt_k = cur_k;
-        advance(nxt_p, nxt_k);
-        const int nxt_keys = tile_keys(nxt_p, nxt_k);
-        if (nxt_keys > 0) load_tile(nxt_p, nxt_k);
-
-        const char* kt = lds + stage * C::STAGE;
+    auto compute = [&](const char* kt, int nkeys, float tscale) {
         const char* vt = kt + C::KTILE;
-        float tscale = qscale_log2;
-        if constexpr (FP8) tscale *= a.k_scale[(int64_t)bh * n + a.col_idx[cur_p]];
-
-        // S^T = K Q^T for the 64 keys (two 32-key halves).
+        // S^T = K Q^T for the 64 keys (two 32-key halves); A fragments read in a batch.
         f32x16 s[2];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-            s[kh] = (f32x16){};
-            const int r = 32 * kh + l32;
-            const char* krow = kt + r * C::KROWB;
+            frag_t kf[C::QSTEPS];
 #pragma unroll
             for (int st = 0; st < C::QSTEPS; ++st) {
                 if constexpr (FP8) {
-                    u32x4 lo = *(const u32x4*)(krow + 16 * swz<C::KCH>(r, 4 * st + 2 * h));
-                    u32x4 hi = *(const u32x4*)(krow + 16 * swz<C::KCH>(r, 4 * st + 2 * h + 1));
-                    i32x8 af = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                    s[kh] = mfma_fp8(af, qf[st], s[kh]);
+                    u32x4 lo = *(const u32x4*)(kt + 32 * kh * C::KROWB + k_rd[2 * st]);
+                    u32x4 hi = *(const u32x4*)(kt + 32 * kh * C::KROWB + k_rd[2 * st + 1]);
+                    kf[st] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                 } else {
-                    bf16x8 af = *(const bf16x8*)(krow + 16 * swz<C::KCH>(r, 2 * st + h));
-                    s[kh] = mfma_bf16(af, qf[st], s[kh]);
+                    kf[st] = *(const bf16x8*)(kt + 32 * kh * C::KROWB + k_rd[st]);
                 }
+            }
+            s[kh] = (f32x16){};
+#pragma unroll
+            for (int st = 0; st < C::QSTEPS; ++st) {
+                if constexpr (FP8) s[kh] = mfma_fp8(kf[st], qf[st], s[kh]);
+                else s[kh] = mfma_bf16(kf[st], qf[st], s[kh]);
             }
         }
 
@@ -247,7 +298,7 @@ attn_kernel(const AttnArgs a) {
                 }
         }
 
-        // Online softmax, log2 domain.
+        // Online softmax, log2 domain, lazily rescaled.
         float mx = s[0][0];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
@@ -257,7 +308,7 @@ attn_kernel(const AttnArgs a) {
         const float mt = mx * tscale;
         if (__any(mt > m_used + 8.0f)) {
             const float m_new = fmaxf(m_used, mt);
-            const float alpha = (m_new == -__builtin_inff()) ? 1.0f : exp2f(m_used - m_new);
+            const float alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_used - m_new);
             m_used = m_new;
             lsum *= alpha;
 #pragma unroll
@@ -269,38 +320,70 @@ attn_kernel(const AttnArgs a) {
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float pv = exp2f(__builtin_fmaf(s[kh][8 * m + e], tscale, -m_used));
-                    lsum += pv;
-                    pb[kh][m][e] = (__bf16)pv;
-                }
+                for (int e = 0; e < 8; ++e)
+                    pb[kh][m][e] = (__bf16)fast_exp2(__builtin_fmaf(s[kh][8 * m + e], tscale, -m_used));
 
-        // O^T += V^T P^T.
-        const int gi = lane & 15;
+        // O^T += V^T P^T, V^T fragments for one 32-row slice of D read in a batch.
 #pragma unroll
         for (int ds = 0; ds < D / 32; ++ds) {
-            const int dcol = 32 * ds + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
-            const int c = dcol >> 3, coff = (dcol & 7) * 2;
+            bf16x8 vf[4];
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+            for (int km = 0; km < 4; ++km) {
+                const int roff = (32 * (km >> 1) + 16 * (km & 1)) * C::VROWB;
+                i16x4 lo = lds_read_tr(vt, roff + v_rd1[ds]);
+                i16x4 hi = lds_read_tr(vt, roff + v_rd2[ds]);
+                i16x4 t8[2] = {lo, hi};
+                vf[km] = *(bf16x8*)t8;
+            }
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const int r1 = 32 * kh + 16 * m + 4 * h + (gi >> 2);
-                    const int r2 = r1 + 8;
-                    i16x4 lo = lds_read_tr(vt, r1 * C::VROWB + 16 * swz<C::VCH>(r1, c) + coff);
-                    i16x4 hi = lds_read_tr(vt, r2 * C::VROWB + 16 * swz<C::VCH>(r2, c) + coff);
-                    i16x4 t8[2] = {lo, hi};
-                    bf16x8 af = *(bf16x8*)t8;
-                    o[ds] = mfma_bf16(af, pb[kh][m], o[ds]);
-                }
+            for (int km = 0; km < 4; ++km) o[ds] = mfma_bf16(vf[km], pb[km >> 1][km & 1], o[ds]);
         }
 
-        if (nxt_keys > 0) store_tile(stage ^ 1);
+        // Row sum of the bf16 weights actually used above (pairs via v_dot2).
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bf16x2 pr = {pb[kh][m][2 * e], pb[kh][m][2 * e + 1]};
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
+                }
+    };
+
+    // ---- main loop: two LDS stages, unrolled by two so stage offsets are immediates -----
+    int cur_p = valid_block(p), cur_k = 0;
+    int nkeys = tile_keys(cur_p, cur_k);
+    if (nkeys > 0) issue_tile(cur_p, cur_k, lds);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    auto tile_scale = [&](int pp) -> float {
+        if constexpr (FP8) return qscale_log2 * entry_kscale(pp);
+        else return qscale_log2;
+    };
+    // One pipeline step: start the next sub-tile's loads into `nxt`, compute on `cur`.
+    // The two stages are passed as restrict pointers so that, once inlined, the LDS reads
+    // and the direct-to-LDS writes carry disjoint alias scopes; without them the wait-count
+    // analysis assumes the reads may see the in-flight writes and waits for every load
+    // before the first read, which would serialise the pipeline.
+    auto step = [&](const char* __restrict__ cur, char* __restrict__ nxt) -> bool {
+        const float ts = tile_scale(cur_p);  // before advance() may move the list window
+        int nxt_p = cur_p, nxt_k = cur_k;
+        advance(nxt_p, nxt_k);
+        const int nxt_keys = tile_keys(nxt_p, nxt_k);
+        if (nxt_keys > 0) issue_tile(nxt_p, nxt_k, nxt);
+        compute(cur, nkeys, ts);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        stage ^= 1;
         cur_p = nxt_p;
         cur_k = nxt_k;
         nkeys = nxt_keys;
+        return nkeys > 0;
+    };
+    while (nkeys > 0) {
+        if (!step(lds, lds + C::STAGE)) break;
+        if (!step(lds + C::STAGE, lds)) break;
     }
 
     // ---- normalise and write --------------------------------------------------------

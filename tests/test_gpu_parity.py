@@ -30,6 +30,8 @@ SMALL = [
     (1, 2, 1, 128, 128, 0.5, None, 0.0, 26),           # a single token
     (1, 2, 50, 128, 128, 1.0, None, 0.0, 27),          # shorter than one block
     (1, 1, 129, 128, 128, 0.5, None, 0.0, 28),         # a one-token last block
+    (1, 1, 4493, 64, 64, 1.0, None, 0.0, 29),          # dense, 71 blocks: lists longer than 64
+    (1, 1, 8453, 64, 128, 1.0, None, 0.0, 30),         # dense, 67 blocks of 128, tail of 5
 ]
 
 
@@ -141,3 +143,29 @@ def test_streams_are_honoured():
     expect = oracle.attention(q, k, v, 128, rp.cpu().numpy(), ci.cpu().numpy())
     mx, mean = errors(to_f64(out), expect)
     assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_forward_long_lists_with_invalid_entries():
+    """Lists longer than 64 entries, padded with many out-of-range entries (skipped)."""
+    B, H, S, D, block = 1, 2, 64 * 75 - 3, 64, 64
+    q, k, v = gen.make_qkv(B, H, S, D, 32)
+    n = oracle.num_blocks(S, block)
+    rows = B * H * n
+    rng = np.random.default_rng(5)
+    good, bad = [], []
+    for r in range(rows):
+        sel = np.sort(rng.choice(n, size=rng.integers(60, n + 1), replace=False)).astype(np.int32)
+        good.append(sel)
+        junk = rng.integers(n, 3 * n, size=rng.integers(0, 80)).astype(np.int32)
+        bad.append(np.concatenate([-junk[: len(junk) // 2], sel, junk[len(junk) // 2:]]).astype(np.int32))
+    rp = np.concatenate([[0], np.cumsum([len(l) for l in good])]).astype(np.int32)
+    ci = np.concatenate(good)
+    rp2 = np.concatenate([[0], np.cumsum([len(l) for l in bad])]).astype(np.int32)
+    ci2 = np.concatenate(bad)
+    expect = oracle.attention(q, k, v, block, rp, ci)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    out = bsa.bsa_forward(dq, dk, dv, block, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda())
+    mx, mean = errors(to_f64(out), expect)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    out2 = bsa.bsa_forward(dq, dk, dv, block, torch.from_numpy(rp2).cuda(), torch.from_numpy(ci2).cuda())
+    assert torch.equal(out, out2)
