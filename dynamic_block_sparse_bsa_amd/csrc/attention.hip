@@ -21,10 +21,8 @@
 //   O^T (D x 32 queries) += V^T . P^T on 32x32x16 bf16 MFMA: P^T comes straight from the
 //   S^T accumulators (converted to bf16), V^T from row-major V tiles in LDS through the
 //   transposing ds_read_b64_tr_b16.
-//   The online softmax works in the log2 domain with a lazily updated running maximum:
-//   the maximum used for the exponent is only raised when a new logit exceeds it by more
-//   than 2^8, which keeps every probability below 256 and leaves the result unchanged
-//   (numerator and denominator share the same reference point).
+//   The online softmax works in the log2 domain with a lazily updated running maximum
+//   (see kRescaleLog2).
 //
 // LDS layout: K and V tiles are row-major [64 keys][D], 16-byte chunks XOR-swizzled per row
 // so that both the K-operand reads (16 rows, one chunk) and the transposing V reads
@@ -45,6 +43,13 @@ constexpr int KT = 64;  // keys per sub-tile
 // s_waitcnt immediate for gfx9-family: vmcnt(0), expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Lazy rescaling of the online softmax: the running maximum used as the exponent's reference
+// point is raised only when a tile's maximum exceeds it by more than this (log2 units), so
+// every probability stays below 2^64 and every fp32 sum below 2^64 * (keys) * |v| -- far from
+// overflow -- while the accumulators are almost never rescaled after the first tile. The
+// result does not depend on the reference point.
+constexpr float kRescaleLog2 = 64.0f;
+
 // 2^x on the transcendental unit (one v_exp_f32). Results below 2^-126 may flush to zero,
 // which is harmless for softmax weights.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -64,6 +69,16 @@ __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
 // fp8 E4M3 x fp8 E4M3, 32x32x64, unit block scales (E8M0 127 = 2^0).
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// max / sum of a value over lanes l and l^32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 typedef short __attribute__((address_space(3))) lds_i16;
@@ -108,7 +123,8 @@ attn_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets stay scalar
     const int h = lane >> 5, l32 = lane & 31;
     const int S = a.S, n = a.n;
 
@@ -280,11 +296,13 @@ attn_kernel(const AttnArgs a) {
                 }
             }
             s[kh] = (f32x16){};
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int st = 0; st < C::QSTEPS; ++st) {
                 if constexpr (FP8) s[kh] = mfma_fp8(kf[st], qf[st], s[kh]);
                 else s[kh] = mfma_bf16(kf[st], qf[st], s[kh]);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
 
         // Mask keys past the end of the sequence (partial last block only).
@@ -304,52 +322,55 @@ attn_kernel(const AttnArgs a) {
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = pair_max(mx);  // lanes l and l^32 hold the two halves of one query column
         const float mt = mx * tscale;
-        if (__any(mt > m_used + 8.0f)) {
-            const float m_new = fmaxf(m_used, mt);
-            const float alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_used - m_new);
-            m_used = m_new;
-            lsum *= alpha;
+        if (__builtin_expect(__any(mt > m_used + kRescaleLog2), 0)) {
+            if (__all(m_used == -__builtin_inff())) {
+                m_used = mt;  // first tile: the accumulators are still zero
+            } else {
+                const float m_new = fmaxf(m_used, mt);
+                const float alpha = fast_exp2(m_used - m_new);
+                m_used = m_new;
+                lsum *= alpha;
 #pragma unroll
-            for (int ds = 0; ds < D / 32; ++ds) o[ds] *= alpha;
+                for (int ds = 0; ds < D / 32; ++ds) o[ds] *= alpha;
+            }
         }
-        bf16x8 pb[2][2];
+        // O^T += V^T P^T, one 16-key k-step at a time: the weights of k-step km (8 per lane)
+        // are formed while the MFMAs of k-step km-1 run, and V^T fragments are read one
+        // k-step ahead.
+        auto read_v = [&](int km, bf16x8 (&vf)[D / 32]) {
+            const int roff = (32 * (km >> 1) + 16 * (km & 1)) * C::VROWB;
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pb[kh][m][e] = (__bf16)fast_exp2(__builtin_fmaf(s[kh][8 * m + e], tscale, -m_used));
-
-        // O^T += V^T P^T, V^T fragments for one 32-row slice of D read in a batch.
-#pragma unroll
-        for (int ds = 0; ds < D / 32; ++ds) {
-            bf16x8 vf[4];
-#pragma unroll
-            for (int km = 0; km < 4; ++km) {
-                const int roff = (32 * (km >> 1) + 16 * (km & 1)) * C::VROWB;
+            for (int ds = 0; ds < D / 32; ++ds) {
                 i16x4 lo = lds_read_tr(vt, roff + v_rd1[ds]);
                 i16x4 hi = lds_read_tr(vt, roff + v_rd2[ds]);
                 i16x4 t8[2] = {lo, hi};
-                vf[km] = *(bf16x8*)t8;
+                vf[ds] = *(bf16x8*)t8;
             }
-#pragma unroll
-            for (int km = 0; km < 4; ++km) o[ds] = mfma_bf16(vf[km], pb[km >> 1][km & 1], o[ds]);
-        }
-
-        // Row sum of the bf16 weights actually used above (pairs via v_dot2).
+        };
         const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+        bf16x8 vcur[D / 32], vnxt[D / 32];
+        read_v(0, vcur);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int km = 0; km < 4; ++km) {
+            bf16x8 pk;
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+            for (int e = 0; e < 8; ++e)
+                pk[e] = (__bf16)fast_exp2(__builtin_fmaf(s[km >> 1][8 * (km & 1) + e], tscale, -m_used));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bf16x2 pr = {pb[kh][m][2 * e], pb[kh][m][2 * e + 1]};
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
-                }
+            for (int e = 0; e < 4; ++e) {
+                bf16x2 pr = {pk[2 * e], pk[2 * e + 1]};
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
+            }
+            if (km < 3) read_v(km + 1, vnxt);
+#pragma unroll
+            for (int ds = 0; ds < D / 32; ++ds) o[ds] = mfma_bf16(vcur[ds], pk, o[ds]);
+            if (km < 3) {
+#pragma unroll
+                for (int ds = 0; ds < D / 32; ++ds) vcur[ds] = vnxt[ds];
+            }
+        }
     };
 
     // ---- main loop: two LDS stages, unrolled by two so stage offsets are immediates -----
@@ -387,7 +408,7 @@ attn_kernel(const AttnArgs a) {
     }
 
     // ---- normalise and write --------------------------------------------------------
-    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float ltot = pair_sum(lsum);
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     if (q_tok < S) {
         __bf16* op = (__bf16*)a.out + (bh_off + q_tok) * D + 4 * h;
