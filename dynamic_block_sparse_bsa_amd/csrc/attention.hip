@@ -21,8 +21,8 @@
 //   O^T (D x 32 queries) += V^T . P^T on 32x32x16 bf16 MFMA: P^T comes straight from the
 //   S^T accumulators (converted to bf16), V^T from row-major V tiles in LDS through the
 //   transposing ds_read_b64_tr_b16.
-//   The online softmax works in the log2 domain with a lazily updated running maximum
-//   (see kRescaleLog2).
+//   The online softmax works in the log2 domain with a lazily raised reference point
+//   (see kSumLimit).
 //
 // LDS layout: K and V tiles are row-major [64 keys][D], 16-byte chunks XOR-swizzled per row
 // so that both the K-operand reads (16 rows, one chunk) and the transposing V reads
@@ -43,12 +43,11 @@ constexpr int KT = 64;  // keys per sub-tile
 // s_waitcnt immediate for gfx9-family: vmcnt(0), expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Lazy rescaling of the online softmax: the running maximum used as the exponent's reference
-// point is raised only when a tile's maximum exceeds it by more than this (log2 units), so
-// every probability stays below 2^64 and every fp32 sum below 2^64 * (keys) * |v| -- far from
-// overflow -- while the accumulators are almost never rescaled after the first tile. The
-// result does not depend on the reference point.
-constexpr float kRescaleLog2 = 64.0f;
+// Lazy rescaling of the online softmax: the reference point of the exponentials is raised
+// only when a query row's running sum of weights would leave (0, kSumLimit], so every weight
+// stays at most 2^64 and every fp32 accumulator far from overflow, while the sub-tile maximum
+// is computed on a row's first sub-tile and almost never after it.
+constexpr float kSumLimit = 0x1p64f;
 
 // 2^x on the transcendental unit (one v_exp_f32). Results below 2^-126 may flush to zero,
 // which is harmless for softmax weights.
@@ -107,12 +106,18 @@ struct Cfg {
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(1))) void* global_void_ptr;
 
-// One 16-byte direct global->LDS load per lane; the wave writes the 1 KiB at lds_dst
-// (wave-uniform) with lane l's data at lds_dst + 16*l.
-__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)lds_dst, 16, 0, 0);
+// One 16-byte direct buffer->LDS load per lane; the wave writes the 1 KiB at lds_dst
+// (wave-uniform) with lane l's data at lds_dst + 16*l. The source is the buffer's base +
+// soff (wave-uniform, a scalar register) + voff (per lane), so a tile's position costs no
+// per-lane address arithmetic.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)lds_dst, 16, voff, soff, 0, 0);
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (word 3: gfx9 default data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
 template <int D, int BLK, bool FP8>
@@ -131,8 +136,8 @@ attn_kernel(const AttnArgs a) {
     const int row = xcd_remap(blockIdx.x, gridDim.x);  // (b*H + h) * n + i
     const int bh = row / n, iq = row - bh * n;
     const int64_t bh_off = (int64_t)bh * S;  // token offset of this (b, h)
-    const char* kbh = (const char*)a.k + bh_off * C::KROWB;
-    const char* vbh = (const char*)a.v + bh_off * C::VROWB;
+    const __amdgpu_buffer_rsrc_t krsrc = buffer_rsrc((const char*)a.k + bh_off * C::KROWB, (uint32_t)S * C::KROWB);
+    const __amdgpu_buffer_rsrc_t vrsrc = buffer_rsrc((const char*)a.v + bh_off * C::VROWB, (uint32_t)S * C::VROWB);
 
     // ---- Q operand (B of S^T = K Q^T), kept in registers --------------------------------
     const int q_tok = iq * BLK + wave * 32 + l32;
@@ -225,28 +230,26 @@ attn_kernel(const AttnArgs a) {
     }
     auto issue_tile = [&](int pp, int kk, char* stage_base) {
         const int key0 = entry(pp) * BLK + kk;
-        const char* kb = kbh + (int64_t)key0 * C::KROWB;
-        const char* vb = vbh + (int64_t)key0 * C::VROWB;
+        const uint32_t ko = (uint32_t)key0 * C::KROWB, vo = (uint32_t)key0 * C::VROWB;
         if (key0 + KT <= S) {
 #pragma unroll
-            for (int x = 0; x < C::KSEGW; ++x) dma16(kb + k_src[x], stage_base + (x * C::NW + wave) * 1024);
+            for (int x = 0; x < C::KSEGW; ++x) dma16(krsrc, k_src[x], ko, stage_base + (x * C::NW + wave) * 1024);
 #pragma unroll
             for (int x = 0; x < C::VSEGW; ++x)
-                dma16(vb + v_src[x], stage_base + C::KTILE + (x * C::NW + wave) * 1024);
+                dma16(vrsrc, v_src[x], vo, stage_base + C::KTILE + (x * C::NW + wave) * 1024);
         } else {  // partial tile: rows past the end re-read the last row (masked later)
             const int last = S - 1 - key0;
 #pragma unroll
             for (int x = 0; x < C::KSEGW; ++x) {
                 const int r = (x * C::NW + wave) * C::KRPS + lane / C::KCH;
                 const int rr = r < last ? r : last;
-                dma16(kb + rr * C::KROWB + (k_src[x] - r * C::KROWB), stage_base + (x * C::NW + wave) * 1024);
+                dma16(krsrc, k_src[x] - (r - rr) * C::KROWB, ko, stage_base + (x * C::NW + wave) * 1024);
             }
 #pragma unroll
             for (int x = 0; x < C::VSEGW; ++x) {
                 const int r = (x * C::NW + wave) * C::VRPS + lane / C::VCH;
                 const int rr = r < last ? r : last;
-                dma16(vb + rr * C::VROWB + (v_src[x] - r * C::VROWB),
-                      stage_base + C::KTILE + (x * C::NW + wave) * 1024);
+                dma16(vrsrc, v_src[x] - (r - rr) * C::VROWB, vo, stage_base + C::KTILE + (x * C::NW + wave) * 1024);
             }
         }
     };
@@ -316,26 +319,40 @@ attn_kernel(const AttnArgs a) {
                 }
         }
 
-        // Online softmax, log2 domain, lazily rescaled.
-        float mx = s[0][0];
+        // Online softmax in the log2 domain. The weights of each 16-key k-step are formed
+        // against the running reference point m_used, and the running sum is checked before
+        // they enter the PV product: only if it leaves (0, kSumLimit] -- on a row's first
+        // sub-tile, where m_used is still -inf, or when scores climb far above m_used -- is
+        // the sub-tile's maximum computed and the reference point raised (the accumulators
+        // rescaled by the same factor). The result does not depend on the reference point.
+        auto form = [&](int km, bf16x8& pk, float& l) {
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+            for (int e = 0; e < 8; ++e)
+                pk[e] = (__bf16)fast_exp2(__builtin_fmaf(s[km >> 1][8 * (km & 1) + e], tscale, -m_used));
+            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
-        mx = pair_max(mx);  // lanes l and l^32 hold the two halves of one query column
-        const float mt = mx * tscale;
-        if (__builtin_expect(__any(mt > m_used + kRescaleLog2), 0)) {
-            if (__all(m_used == -__builtin_inff())) {
-                m_used = mt;  // first tile: the accumulators are still zero
-            } else {
-                const float m_new = fmaxf(m_used, mt);
-                const float alpha = fast_exp2(m_used - m_new);
-                m_used = m_new;
-                lsum *= alpha;
-#pragma unroll
-                for (int ds = 0; ds < D / 32; ++ds) o[ds] *= alpha;
+            for (int e = 0; e < 4; ++e) {
+                bf16x2 pr = {pk[2 * e], pk[2 * e + 1]};
+                l = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l, false);
             }
-        }
+        };
+        auto raise_reference = [&]() {
+            float mx = s[0][0];
+            // Opaque to the optimiser, so that the maximum below stays on this rare path
+            // instead of being merged across call sites and hoisted into the common one.
+            asm volatile("" : "+v"(mx));
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
+            mx = pair_max(mx);  // lanes l and l^32 hold the two halves of one query column
+            const float m_new = fmaxf(m_used, mx * tscale);
+            const float alpha = fast_exp2(m_used - m_new);  // 0 on the first sub-tile
+            m_used = m_new;
+            lsum *= alpha;
+#pragma unroll
+            for (int ds = 0; ds < D / 32; ++ds) o[ds] *= alpha;
+        };
         // O^T += V^T P^T, one 16-key k-step at a time: the weights of k-step km (8 per lane)
         // are formed while the MFMAs of k-step km-1 run, and V^T fragments are read one
         // k-step ahead.
@@ -349,20 +366,19 @@ attn_kernel(const AttnArgs a) {
                 vf[ds] = *(bf16x8*)t8;
             }
         };
-        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
         bf16x8 vcur[D / 32], vnxt[D / 32];
         read_v(0, vcur);
 #pragma unroll
         for (int km = 0; km < 4; ++km) {
             bf16x8 pk;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pk[e] = (__bf16)fast_exp2(__builtin_fmaf(s[km >> 1][8 * (km & 1) + e], tscale, -m_used));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bf16x2 pr = {pk[2 * e], pk[2 * e + 1]};
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
+            float lnew = lsum;
+            form(km, pk, lnew);
+            if (__builtin_expect(__any(!(lnew <= kSumLimit)), 0)) {
+                raise_reference();
+                lnew = lsum;
+                form(km, pk, lnew);
             }
+            lsum = lnew;
             if (km < 3) read_v(km + 1, vnxt);
 #pragma unroll
             for (int ds = 0; ds < D / 32; ++ds) o[ds] = mfma_bf16(vcur[ds], pk, o[ds]);

@@ -169,3 +169,32 @@ def test_forward_long_lists_with_invalid_entries():
     assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
     out2 = bsa.bsa_forward(dq, dk, dv, block, torch.from_numpy(rp2).cuda(), torch.from_numpy(ci2).cuda())
     assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("D,block", [(128, 128), (64, 64), (64, 128)])
+def test_forward_rising_scores(D, block):
+    """Row maxima that climb by about 75 log2 units from one key block to the next, so the
+    kernel raises its reference point mid-row on every block; in the reversed order the
+    first block sets it once and the weights of the last blocks underflow to zero."""
+    B, H, S = 1, 2, 8 * block - 30
+    q, k, v = gen.make_qkv(B, H, S, D, 33)
+    n = oracle.num_blocks(S, block)
+    kk = gen.bf16_bits_to_f32(k).astype(np.float64)
+    for j in range(n):
+        sign = -1.0 if j == 3 else 1.0  # a sign flip changes which keys score highest
+        kk[:, :, j * block:(j + 1) * block, :] *= sign * (1.0 + 20.0 * j)
+    k = gen.f32_to_bf16_bits(kk.astype(np.float32))
+    rows = B * H * n
+    rp = (np.arange(rows + 1) * n).astype(np.int32)
+    ci = np.tile(np.arange(n, dtype=np.int32), rows)
+    expect = oracle.attention(q, k, v, block, rp, ci)
+    out = bsa.bsa_forward(to_dev(q), to_dev(k), to_dev(v), block, torch.from_numpy(rp).cuda(),
+                          torch.from_numpy(ci).cuda())
+    mx, mean = errors(to_f64(out), expect)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    # reversed lists: the largest scores come first, the reference point is set once
+    ci_rev = np.tile(np.arange(n - 1, -1, -1, dtype=np.int32), rows)
+    out_rev = bsa.bsa_forward(to_dev(q), to_dev(k), to_dev(v), block, torch.from_numpy(rp).cuda(),
+                              torch.from_numpy(ci_rev).cuda())
+    mx, mean = errors(to_f64(out_rev), expect)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
