@@ -196,23 +196,6 @@ attn_kernel(const AttnArgs a) {
         }
         return pend;
     };
-    // Sub-tile cursor: (list position, key offset inside the block).
-    auto tile_keys = [&](int pp, int kk) -> int {  // valid keys in sub-tile, 0 at the end
-        if (pp >= pend) return 0;
-        int j = entry(pp);
-        int rem = S - (j * BLK + kk);
-        int inblk = BLK - kk;
-        int nk = rem < inblk ? rem : inblk;
-        return nk < KT ? nk : KT;
-    };
-    auto advance = [&](int& pp, int& kk) {
-        int j = entry(pp);
-        int next = kk + KT;
-        if (next < BLK && j * BLK + next < S) { kk = next; return; }
-        kk = 0;
-        pp = valid_block(pp + 1);
-    };
-
     // ---- direct global->LDS tile loads ------------------------------------------------
     // Segment sg of a tile holds rows [sg*RPS, (sg+1)*RPS); lane l fills slot l % CH of row
     // sg*RPS + l / CH, i.e. it fetches chunk (slot ^ swz(row)) of that row, so the tile
@@ -228,17 +211,18 @@ attn_kernel(const AttnArgs a) {
         const int r = (x * C::NW + wave) * C::VRPS + lane / C::VCH;
         v_src[x] = r * C::VROWB + 16 * swz<C::VCH>(r, lane % C::VCH);
     }
-    auto issue_tile = [&](int pp, int kk, char* stage_base) {
-        const int key0 = entry(pp) * BLK + kk;
+    // Loads the sub-tile of nk keys (1 <= nk <= KT) starting at key0. Rows past the end of
+    // the sequence re-read its last row; their scores are masked.
+    auto issue_tile = [&](int key0, int nk, char* stage_base) {
         const uint32_t ko = (uint32_t)key0 * C::KROWB, vo = (uint32_t)key0 * C::VROWB;
-        if (key0 + KT <= S) {
+        if (nk == KT) {
 #pragma unroll
             for (int x = 0; x < C::KSEGW; ++x) dma16(krsrc, k_src[x], ko, stage_base + (x * C::NW + wave) * 1024);
 #pragma unroll
             for (int x = 0; x < C::VSEGW; ++x)
                 dma16(vrsrc, v_src[x], vo, stage_base + C::KTILE + (x * C::NW + wave) * 1024);
-        } else {  // partial tile: rows past the end re-read the last row (masked later)
-            const int last = S - 1 - key0;
+        } else {
+            const int last = nk - 1;
 #pragma unroll
             for (int x = 0; x < C::KSEGW; ++x) {
                 const int r = (x * C::NW + wave) * C::KRPS + lane / C::KCH;
@@ -280,7 +264,7 @@ attn_kernel(const AttnArgs a) {
     float m_used = -__builtin_inff();
     float lsum = 0.0f;
 
-    auto compute = [&](const char* kt, int nkeys, float tscale) {
+    auto compute = [&](const char* kt, int nkeys, float tscale) __attribute__((always_inline)) {
         const char* vt = kt + C::KTILE;
         // S^T = K Q^T for the 64 keys (two 32-key halves); A fragments read in a batch.
         f32x16 s[2];
@@ -389,38 +373,65 @@ attn_kernel(const AttnArgs a) {
         }
     };
 
-    // ---- main loop: two LDS stages, unrolled by two so stage offsets are immediates -----
-    int cur_p = valid_block(p), cur_k = 0;
-    int nkeys = tile_keys(cur_p, cur_k);
-    if (nkeys > 0) issue_tile(cur_p, cur_k, lds);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    auto tile_scale = [&](int pp) -> float {
+    // ---- main loop: the list a block at a time, two LDS stages ------------------------
+    // A 128-token block is two 64-key sub-tiles: the first is computed from stage 0 while the
+    // second loads into stage 1, and the second from stage 1 while the next block's first
+    // loads into stage 0 (a 64-token block is one sub-tile, and blocks alternate stages).
+    // Stage offsets are therefore immediates, and the per-step list work is one lookup.
+    auto keys_at = [&](int key0) -> int {  // keys of the sub-tile at key0 (<= 0: none)
+        const int r = S - key0;
+        return r < KT ? r : KT;
+    };
+    auto block_scale = [&](int pp) -> float {  // logit scale of list entry pp (window current)
         if constexpr (FP8) return qscale_log2 * entry_kscale(pp);
         else return qscale_log2;
     };
-    // One pipeline step: start the next sub-tile's loads into `nxt`, compute on `cur`.
-    // The two stages are passed as restrict pointers so that, once inlined, the LDS reads
-    // and the direct-to-LDS writes carry disjoint alias scopes; without them the wait-count
-    // analysis assumes the reads may see the in-flight writes and waits for every load
-    // before the first read, which would serialise the pipeline.
-    auto step = [&](const char* __restrict__ cur, char* __restrict__ nxt) -> bool {
-        const float ts = tile_scale(cur_p);  // before advance() may move the list window
-        int nxt_p = cur_p, nxt_k = cur_k;
-        advance(nxt_p, nxt_k);
-        const int nxt_keys = tile_keys(nxt_p, nxt_k);
-        if (nxt_keys > 0) issue_tile(nxt_p, nxt_k, nxt);
-        compute(cur, nkeys, ts);
+    int pos = valid_block(p);
+    int j = pos < pend ? entry(pos) : -1;
+    float ts = j >= 0 ? block_scale(pos) : 0.0f;
+    if (j >= 0) issue_tile(j * BLK, keys_at(j * BLK), lds);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    // Advances to the next block in the list (j = -1 at the end).
+    auto next_block = [&]() {
+        pos = valid_block(pos + 1);
+        j = pos < pend ? entry(pos) : -1;
+        if (j >= 0) ts = block_scale(pos);
+    };
+    // One step: start loading `load_nk` keys at load_key0 into `nxt` (if load_nk > 0) and
+    // compute the sub-tile in `cur` (if nkeys > 0). The stages are restrict pointers so that,
+    // once inlined, the LDS reads and the direct-to-LDS writes carry disjoint alias scopes;
+    // without them the wait-count analysis assumes the reads may see the in-flight writes
+    // and waits for every load before the first read, which would serialise the pipeline.
+    auto step = [&](const char* __restrict__ cur, char* __restrict__ nxt, int nkeys, float tsc,
+                    int load_key0, int load_nk) __attribute__((always_inline)) {
+        if (load_nk > 0) issue_tile(load_key0, load_nk, nxt);
+        if (nkeys > 0) compute(cur, nkeys, tsc);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        cur_p = nxt_p;
-        cur_k = nxt_k;
-        nkeys = nxt_keys;
-        return nkeys > 0;
     };
-    while (nkeys > 0) {
-        if (!step(lds, lds + C::STAGE)) break;
-        if (!step(lds + C::STAGE, lds)) break;
+    if constexpr (BLK == 2 * KT) {
+        while (j >= 0) {
+            const int key0 = j * BLK;
+            const int nk0 = keys_at(key0), nk1 = keys_at(key0 + KT);
+            const float tsb = ts;
+            step(lds, lds + C::STAGE, nk0, tsb, key0 + KT, nk1);
+            next_block();
+            step(lds + C::STAGE, lds, nk1, tsb, j * BLK, j >= 0 ? keys_at(j * BLK) : 0);
+        }
+    } else {
+        static_assert(BLK == KT, "blocks of one or two sub-tiles");
+        while (j >= 0) {
+            int nk = keys_at(j * BLK);
+            float tsb = ts;
+            next_block();
+            step(lds, lds + C::STAGE, nk, tsb, j * BLK, j >= 0 ? keys_at(j * BLK) : 0);
+            if (j < 0) break;
+            nk = keys_at(j * BLK);
+            tsb = ts;
+            next_block();
+            step(lds + C::STAGE, lds, nk, tsb, j * BLK, j >= 0 ? keys_at(j * BLK) : 0);
+        }
     }
 
     // ---- normalise and write --------------------------------------------------------
