@@ -82,6 +82,75 @@ def cpu_baseline(q, k, v, cfg, budget_tokens):
     }
 
 
+SWEEP_RATIOS = (0.10, 0.125, 0.15, 0.175, 0.20)
+
+
+def sweep(args):
+    """keep_ratio sweep over the pages' 10-20 % range on each shape: the same select and forward
+    kernels, timed per call, with the output compared against dense attention (keep_ratio 1,
+    every key block) computed by the same forward kernel on the same inputs."""
+    import torch
+
+    import dynamic_block_sparse_bsa_amd as bsa
+    import gen
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    reps = max(2, args.steps // 4)
+    for name in ("480p", "720p", "long"):
+        q, k, v, cfg = gen.make_config(name)
+        B, H, S, D = q.shape
+        block = cfg["block"]
+        to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        del q, k, v
+        n = bsa.bsa_num_blocks(S, block)
+        rows = B * H * n
+        rp1 = torch.arange(rows + 1, dtype=torch.int32, device=dev) * n
+        ci1 = torch.arange(n, dtype=torch.int32, device=dev).repeat(rows)
+        dense = bsa.bsa_forward(qd, kd, vd, block, rp1, ci1)
+        del rp1, ci1
+        dense_f = dense.float()
+        dense_norm = float(torch.linalg.vector_norm(dense_f))
+        out = torch.empty_like(qd)
+        for r in SWEEP_RATIOS:
+            kept = bsa.bsa_num_kept(n, r)
+            rp, ci = bsa.bsa_select(qd, kd, block, r)
+            for _ in range(args.warmup):
+                bsa.bsa_select(qd, kd, block, r, row_ptr=rp, col_idx=ci)
+                bsa.bsa_forward(qd, kd, vd, block, rp, ci, out=out)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
+            for _ in range(reps):
+                bsa.bsa_select(qd, kd, block, r, row_ptr=rp, col_idx=ci)
+            ev[1].record()
+            for _ in range(reps):
+                bsa.bsa_forward(qd, kd, vd, block, rp, ci, out=out)
+            ev[2].record()
+            torch.cuda.synchronize()
+            sel_ms = ev[0].elapsed_time(ev[1]) / reps
+            fwd_ms = ev[1].elapsed_time(ev[2]) / reps
+            flop = 4.0 * D * kept_flops(rp.cpu().numpy(), ci.cpu().numpy(), S, block)
+            diff = out.float() - dense_f
+            line = {
+                "workload": "%s: B=%d H=%d S=%d D=%d block=%d" % (name, B, H, S, D, block),
+                "keep_ratio": r, "kept_blocks": kept, "n_blocks": n,
+                "select_ms": round(sel_ms, 4), "attention_ms": round(fwd_ms, 4),
+                "kept_tflops": round(flop / (fwd_ms * 1e-3) / 1e12, 1),
+                "frac_bf16_mfma_peak": round(flop / (fwd_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "vs_dense_max_abs": round(float(diff.abs().max()), 5),
+                "vs_dense_mean_abs": round(float(diff.abs().mean()), 6),
+                "vs_dense_rel_l2": round(float(torch.linalg.vector_norm(diff)) / dense_norm, 5),
+            }
+            print(json.dumps(line), flush=True)
+            del diff, rp, ci
+        del qd, kd, vd, dense, dense_f, out
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,11 +162,17 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (PMC calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="keep_ratio sweep 0.10-0.20 on the 480p, 720p and long shapes instead: one "
+                         "JSON line per point with ms, kept TFLOP/s and the error against dense attention")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the design notes "
               "describe how the work would shard by head).", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
 
     import torch
 

@@ -198,3 +198,31 @@ def test_forward_rising_scores(D, block):
                               torch.from_numpy(ci_rev).cuda())
     mx, mean = errors(to_f64(out_rev), expect)
     assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+
+
+SWEEP_RATIOS = (0.10, 0.125, 0.15, 0.175, 0.20)
+
+
+def test_keep_ratio_sweep():
+    """The pages' 10-20 % keep range on one locality-structured shape: lists and outputs match
+    the oracle at every ratio, and the distance to dense attention does not grow as more key
+    blocks are kept."""
+    B, H, S, D, block = 1, 2, 4000, 128, 128
+    q, k, v = gen.make_qkv(B, H, S, D, 34, grid=(10, 20, 20), alpha=0.5)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    n = oracle.num_blocks(S, block)
+    rows = B * H * n
+    rp1 = torch.arange(rows + 1, dtype=torch.int32, device=qd.device) * n
+    ci1 = torch.arange(n, dtype=torch.int32, device=qd.device).repeat(rows)
+    dense = to_f64(bsa.bsa_forward(qd, kd, vd, block, rp1, ci1))
+    dist = []
+    for r in SWEEP_RATIOS:
+        rp, ci = bsa.bsa_select(qd, kd, block, r)
+        ref = oracle.select(q, k, block, r)
+        check_lists(rp.cpu().numpy(), ci.cpu().numpy(), ref)
+        out = to_f64(bsa.bsa_forward(qd, kd, vd, block, rp, ci))
+        expect = oracle.attention(q, k, v, block, rp.cpu().numpy(), ci.cpu().numpy())
+        mx, mean = errors(out, expect)
+        assert mx <= BF16_MAX and mean <= BF16_MEAN, (r, mx, mean)
+        dist.append(float(np.mean(np.abs(out - dense))))
+    assert dist[-1] <= dist[0], dist
