@@ -55,6 +55,10 @@ def _load():
     lib.oracle_quantize_fp8.argtypes = [P, i32, i32, i32, i32, i32, P, P]
     lib.oracle_attention_fp8.restype = None
     lib.oracle_attention_fp8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, i64, P]
+    lib.oracle_quantize_v_fp8.restype = None
+    lib.oracle_quantize_v_fp8.argtypes = [P, i32, i32, i32, i32, P, P]
+    lib.oracle_attention_fp8_full.restype = None
+    lib.oracle_attention_fp8_full.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, i64, P]
     _lib = lib
     return lib
 
@@ -211,4 +215,41 @@ def attention_fp8(q8, q_scale, k8, k_scale, v, block: int, row_ptr, col_idx, tok
     out = np.empty(((B * H * S) if t is None else nt, D), dtype=np.float64)
     _load().oracle_attention_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), B, H,
                                  S, D, block, _ptr(row_ptr), _ptr(col_idx), _ptr(t), nt, _ptr(out))
+    return out.reshape(B, H, S, D) if t is None else out
+
+
+def quantize_v_fp8(v):
+    """(codes uint8 [B,H,S,D], scale float32 [B,H,D]): one scale per (batch, head, channel)
+    over the whole sequence, the full FP8 path's reading for V."""
+    v = _bf16_tensor(v)
+    B, H, S, D = v.shape
+    codes = np.empty((B, H, S, D), dtype=np.uint8)
+    scale = np.empty((B, H, D), dtype=np.float32)
+    _load().oracle_quantize_v_fp8(_ptr(v), B, H, S, D, _ptr(codes), _ptr(scale))
+    return codes, scale
+
+
+def attention_fp8_full(q8, q_scale, k8, k_scale, v8, v_scale, block: int, row_ptr, col_idx, tokens=None):
+    """The full FP8 path: Q, K (per-block scales) and V (per-channel scales) as E4M3 codes,
+    online softmax over 64-key sub-tiles in list order with the weights stored as E4M3."""
+    q8 = np.ascontiguousarray(q8, dtype=np.uint8)
+    k8 = np.ascontiguousarray(k8, dtype=np.uint8)
+    v8 = np.ascontiguousarray(v8, dtype=np.uint8)
+    if q8.ndim != 4 or k8.shape != q8.shape or v8.shape != q8.shape:
+        raise ValueError("fp8 operand shapes do not match")
+    B, H, S, D = q8.shape
+    n = num_blocks(S, block)
+    q_scale = np.ascontiguousarray(q_scale, dtype=np.float32)
+    k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+    v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+    if q_scale.size != B * H * n or k_scale.size != B * H * n or v_scale.size != B * H * D:
+        raise ValueError("scale shapes do not match")
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
+    if row_ptr.size != B * H * n + 1 or row_ptr[-1] > col_idx.size:
+        raise ValueError("row_ptr / col_idx do not describe B*H*n rows")
+    t, nt = _tokens_arg(tokens)
+    out = np.empty(((B * H * S) if t is None else nt, D), dtype=np.float64)
+    _load().oracle_attention_fp8_full(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale),
+                                      B, H, S, D, block, _ptr(row_ptr), _ptr(col_idx), _ptr(t), nt, _ptr(out))
     return out.reshape(B, H, S, D) if t is None else out

@@ -28,6 +28,12 @@
  *   - a query block with an empty kept list produces a zero output row;
  *   - FP8 is OCP E4M3FN with round-to-nearest-even, one fp32 scale = absmax/448 per
  *     (batch, head, token block) for Q and for K separately (scale 1 when absmax=0).
+ *   - Full FP8 path (P and V in E4M3 as well; the pages name SageAttention2 but give
+ *     none of its steps): V has one fp32 scale per (batch, head, channel) over the whole
+ *     sequence; the softmax runs online over the kept keys in list order, 64 keys at a
+ *     time, and each 64-key sub-tile's weights 2^(x - m) <= 1 (x the logit in log2 units,
+ *     m the running maximum after that sub-tile) are stored as E4M3FN codes of 448 times
+ *     the weight; the normaliser is the sum of the stored weights.
  *
  * Layouts: tensors are [B, H, S, D] row-major; bf16 values are passed as their raw
  * 16-bit patterns. Block i of a sequence is tokens [i*block, min(S,(i+1)*block)).
@@ -277,4 +283,103 @@ void oracle_attention_fp8(const uint8_t* q8, const float* q_scale, const uint8_t
              V = {v, NULL, NULL, S, D, block, n};
     if (!tokens) ntok = (int64_t)B * H * S;
     attention_core(&Q, &K, &V, (int64_t)B * H, row_ptr, col_idx, tokens, ntok, out);
+}
+
+/* ---- Full FP8 path: P and V in E4M3 as well -------------------------------------------
+ * [KC] 动态稀疏量化注意力 and [AO] step 3: the sparse path is combined with SageAttention2
+ * into an FP8 attention path. The quantisation steps below are this implementation's
+ * reading (see the header): they are not on the pages. */
+
+/* Per (batch*head, channel d): scale = absmax over all S tokens / 448 in fp32 (1 when the
+ * channel is all zero); code = nearest E4M3FN to v/scale, the division in IEEE fp32.
+ * codes keep the [B, H, S, D] layout of v. */
+void oracle_quantize_v_fp8(const uint16_t* v, int32_t B, int32_t H, int32_t S, int32_t D,
+                           uint8_t* codes, float* scale /* [B*H, D] */) {
+    int64_t BH = (int64_t)B * H;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < BH * D; ++r) {
+        int64_t bh = r / D, d = r % D;
+        float amax = 0.0f;
+        for (int64_t t = 0; t < S; ++t) {
+            float a = fabsf((float)bf16_value(v[(bh * S + t) * D + d]));
+            if (a > amax) amax = a;
+        }
+        float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+        scale[r] = sc;
+        for (int64_t t = 0; t < S; ++t) {
+            int64_t off = (bh * S + t) * D + d;
+            float y = (float)bf16_value(v[off]) / sc;
+            codes[off] = oracle_e4m3_encode((double)y);
+        }
+    }
+}
+
+/* Attention with Q, K (per-block scales) and V (per-channel scales) as E4M3 codes and the
+ * softmax weights stored as E4M3 as well. For every requested query token t of query
+ * block i: walk the kept blocks of row i in list order; split each block's keys into
+ * sub-tiles of 64 (the last may be shorter); for each sub-tile
+ *   x_u   = (q_t . k_u) log2(e) / sqrt(D)              (dequantised codes, fp64)
+ *   m'    = max(m, max_u x_u);  O *= 2^(m - m'),  l *= 2^(m - m')   (0 while m = -inf)
+ *   w_u   = value(E4M3(448 * 2^(x_u - m'))) / 448
+ *   l    += sum_u w_u;  O += sum_u w_u v_u             (v_u dequantised)
+ *   m     = m'
+ * and return O / l (zeros for an empty list). Entries outside [0, n) are skipped. */
+void oracle_attention_fp8_full(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                               const float* k_scale, const uint8_t* v8, const float* v_scale,
+                               int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                               const int32_t* row_ptr, const int32_t* col_idx,
+                               const int64_t* tokens, int64_t ntok, double* out) {
+    const int64_t n = oracle_num_blocks(S, block), KT = 64;
+    const double log2e = 1.4426950408889634073599, inv = 1.0 / sqrt((double)D);
+    if (!tokens) ntok = (int64_t)B * H * S;
+#pragma omp parallel
+    {
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+        double* x = (double*)malloc(sizeof(double) * (size_t)KT);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t mi = 0; mi < ntok; ++mi) {
+            int64_t flat = tokens ? tokens[mi] : mi;
+            int64_t bh = flat / S, t = flat % S, row = bh * n + t / block;
+            double* o = out + mi * D;
+            double qs = (double)q_scale[bh * n + t / block];
+            for (int64_t d = 0; d < D; ++d) {
+                qrow[d] = oracle_e4m3_value(q8[(bh * S + t) * D + d]) * qs;
+                o[d] = 0.0;
+            }
+            double m = -INFINITY, l = 0.0;
+            for (int32_t p = row_ptr[row]; p < row_ptr[row + 1]; ++p) {
+                int64_t j = col_idx[p];
+                if (j < 0 || j >= n) continue;
+                double ks = (double)k_scale[bh * n + j];
+                int64_t u_end = (j + 1) * block < S ? (j + 1) * block : S;
+                for (int64_t u0 = j * block; u0 < u_end; u0 += KT) {
+                    int64_t u1 = u0 + KT < u_end ? u0 + KT : u_end;
+                    double mt = -INFINITY;
+                    for (int64_t u = u0; u < u1; ++u) {
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            dot += qrow[d] * oracle_e4m3_value(k8[(bh * S + u) * D + d]) * ks;
+                        x[u - u0] = dot * inv * log2e;
+                        if (x[u - u0] > mt) mt = x[u - u0];
+                    }
+                    double m_new = mt > m ? mt : m;
+                    double alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
+                    l *= alpha;
+                    for (int64_t d = 0; d < D; ++d) o[d] *= alpha;
+                    for (int64_t u = u0; u < u1; ++u) {
+                        double w = oracle_e4m3_value(oracle_e4m3_encode(448.0 * exp2(x[u - u0] - m_new))) / 448.0;
+                        l += w;
+                        for (int64_t d = 0; d < D; ++d)
+                            o[d] += w * oracle_e4m3_value(v8[(bh * S + u) * D + d]) * (double)v_scale[bh * D + d];
+                    }
+                    m = m_new;
+                }
+            }
+            if (l > 0.0)
+                for (int64_t d = 0; d < D; ++d) o[d] /= l;
+            else
+                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        }
+        free(qrow); free(x);
+    }
 }

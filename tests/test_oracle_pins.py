@@ -367,3 +367,172 @@ def test_fp8_exact_inputs_reduce_to_bf16_attention():
     a = oracle.attention(q, k, v, block, sel["row_ptr"], sel["col_idx"])
     b = oracle.attention_fp8(q8, qs, k8, ks, v, block, sel["row_ptr"], sel["col_idx"])
     assert np.max(np.abs(a - b)) <= 1e-13
+
+
+# ---- full FP8 path: P and V in E4M3 as well --------------------------------------------
+
+def e4m3_round(x):
+    """Library rounding to E4M3FN (torch's cast), back to fp64."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def dequant(codes, scale_bcast):
+    return torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale_bcast
+
+
+def full_fp8_inputs(B, H, S, D, block, seed, qzero=False):
+    q, k, v = gen.make_qkv(B, H, S, D, seed)
+    if qzero:
+        q = np.zeros_like(q)
+    q8, qs = oracle.quantize_fp8(q, block)
+    k8, ks = oracle.quantize_fp8(k, block)
+    v8, vs = oracle.quantize_v_fp8(v)
+    return q, k, v, q8, qs, k8, ks, v8, vs
+
+
+def test_quantize_v_fp8_matches_torch_cast():
+    B, H, S, D = 1, 2, 300, 32
+    _, _, v = gen.make_qkv(B, H, S, D, 40)
+    v[0, 1, :, 5] = 0  # an all-zero channel gets scale 1
+    codes, scale = oracle.quantize_v_fp8(v)
+    vf = f32(v)
+    amax = np.max(np.abs(vf), axis=2)  # [B, H, D]
+    expect = np.where(amax > 0, amax.astype(np.float32) / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    assert np.array_equal(scale, expect)
+    ref = torch.from_numpy((vf / scale[:, :, None, :]).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    assert np.all(codes[0, 1, :, 5] == 0)
+
+
+def test_fp8_full_constant_v_gives_constant_output():
+    # Each channel of V constant: its codes are exactly +-448 and the stored weights,
+    # whatever their rounding, normalise to one, so every output row equals V's dequantised
+    # row (448 times the fp32 scale; within a few ulp of V itself).
+    B, H, S, D, block = 1, 2, 333, 64, 128
+    _, _, _, q8, qs, k8, ks, _, _ = full_fp8_inputs(B, H, S, D, block, 41)
+    rng = np.random.default_rng(41)
+    c = bf16(rng.normal(0, 2, size=(B, H, 1, D)).astype(np.float32))
+    v = np.broadcast_to(c, (B, H, S, D)).copy()
+    v8, vs = oracle.quantize_v_fp8(v)
+    n = oracle.num_blocks(S, block)
+    sel = oracle.select(*gen.make_qkv(B, H, S, D, 41)[:2], block, 0.5)
+    out = oracle.attention_fp8_full(q8, qs, k8, ks, v8, vs, block, sel["row_ptr"], sel["col_idx"])
+    assert np.all(v8 & 0x7F == 0x7E)
+    vhat = dequant(v8, vs[:, :, None, :].astype(np.float64))
+    assert np.max(np.abs(out - vhat)) <= 1e-12
+    assert np.max(np.abs(vhat - f32(c))) <= 1e-6
+    assert n == 3
+
+
+def test_fp8_full_equal_logits_average_v():
+    # Q = 0: every logit is 0, every stored weight is exactly 1 (448 is an E4M3 value), so
+    # each output row is the plain average of dequantised V over the row's kept keys.
+    B, H, S, D, block = 1, 2, 300, 32, 64
+    q, k, v, q8, qs, k8, ks, v8, vs = full_fp8_inputs(B, H, S, D, block, 42, qzero=True)
+    sel = oracle.select(gen.make_qkv(B, H, S, D, 42)[0], k, block, 0.4)
+    out = oracle.attention_fp8_full(q8, qs, k8, ks, v8, vs, block, sel["row_ptr"], sel["col_idx"])
+    vhat = dequant(v8, vs[:, :, None, :].astype(np.float64))
+    n = oracle.num_blocks(S, block)
+    rp, ci = sel["row_ptr"], sel["col_idx"]
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        for i in range(n):
+            keys = np.concatenate([np.arange(j * block, min(S, (j + 1) * block)) for j in ci[rp[bh * n + i]:rp[bh * n + i + 1]]])
+            mean = vhat[b, h, keys].mean(axis=0)
+            rows = out[b, h, i * block:min(S, (i + 1) * block)]
+            assert np.max(np.abs(rows - mean)) <= 1e-12
+
+
+def test_fp8_full_reduces_to_direct_formula_when_the_first_sub_tile_holds_the_max():
+    # Key u (u < 64) is a large multiple of query u, so for queries 0..63 the row maximum
+    # sits in the first 64-key sub-tile of the first kept block: the running maximum never
+    # moves afterwards and the method reduces to w_u = E4M3(448 * 2^(x_u - x_max)) / 448,
+    # O = sum w v / sum w, computed here with torch's E4M3 cast and decode.
+    B, H, S, D, block = 1, 1, 256, 64, 128
+    q, k, v = gen.make_qkv(B, H, S, D, 43)
+    kf = f32(k)
+    kf[0, 0, :64] = 3.0 * f32(q)[0, 0, :64]
+    k = bf16(kf)
+    q8, qs = oracle.quantize_fp8(q, block)
+    k8, ks = oracle.quantize_fp8(k, block)
+    v8, vs = oracle.quantize_v_fp8(v)
+    n = oracle.num_blocks(S, block)
+    rp = np.array([0, 2, 4], np.int32)
+    ci = np.array([0, 1, 0, 1], np.int32)
+    tokens = np.arange(64)
+    out = oracle.attention_fp8_full(q8, qs, k8, ks, v8, vs, block, rp, ci, tokens=tokens)
+    qhat = dequant(q8, np.repeat(qs, block, axis=2)[:, :, :S, None].astype(np.float64))[0, 0]
+    khat = dequant(k8, np.repeat(ks, block, axis=2)[:, :, :S, None].astype(np.float64))[0, 0]
+    vhat = dequant(v8, vs[:, :, None, :].astype(np.float64))[0, 0]
+    x = (qhat[:64] @ khat.T) * math.log2(math.e) / math.sqrt(D)  # [64 queries, S keys]
+    assert np.all(np.argmax(x, axis=1) == np.arange(64))
+    w = e4m3_round(448.0 * np.exp2(x - x.max(axis=1, keepdims=True))) / 448.0
+    expect = (w @ vhat) / w.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(out - expect)) <= 1e-12
+    assert n == 2
+
+
+def test_fp8_full_within_weight_rounding_bound_of_exact_softmax():
+    # Against the exact softmax over the same dequantised Q, K and V, the only difference is
+    # the E4M3 rounding of each weight: at most 2^-4 relative for normal values, so the output
+    # can move by at most 2 * 2^-4 / (1 - 2^-4) of max |v| (plus a subnormal term that is far
+    # smaller here). A dropped or inverted rescale of the earlier sub-tiles, or weights taken
+    # against a stale maximum, breaks this by orders of magnitude.
+    B, H, S, D, block = 1, 2, 400, 64, 64
+    q, k, v, q8, qs, k8, ks, v8, vs = full_fp8_inputs(B, H, S, D, block, 44)
+    kf = f32(k)
+    for j in range(oracle.num_blocks(S, block)):  # rising logits: the maximum moves often
+        kf[:, :, j * block:(j + 1) * block] *= 1.0 + 0.6 * j
+    k = bf16(kf)
+    k8, ks = oracle.quantize_fp8(k, block)
+    sel = oracle.select(q, k, block, 0.5)
+    rp, ci = sel["row_ptr"], sel["col_idx"]
+    out = oracle.attention_fp8_full(q8, qs, k8, ks, v8, vs, block, rp, ci)
+    n = oracle.num_blocks(S, block)
+    qhat = dequant(q8, np.repeat(qs, block, axis=2)[:, :, :S, None].astype(np.float64))
+    khat = dequant(k8, np.repeat(ks, block, axis=2)[:, :, :S, None].astype(np.float64))
+    vhat = dequant(v8, vs[:, :, None, :].astype(np.float64))
+    bound = 2 * 2.0 ** -4 / (1 - 2.0 ** -4) * np.max(np.abs(vhat)) + 1e-3
+    worst = 0.0
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        for i in range(n):
+            keys = np.concatenate([np.arange(j * block, min(S, (j + 1) * block)) for j in ci[rp[bh * n + i]:rp[bh * n + i + 1]]])
+            qi = qhat[b, h, i * block:min(S, (i + 1) * block)]
+            x = qi @ khat[b, h, keys].T / math.sqrt(D)
+            p = np.exp(x - x.max(axis=1, keepdims=True))
+            exact = (p / p.sum(axis=1, keepdims=True)) @ vhat[b, h, keys]
+            worst = max(worst, float(np.max(np.abs(out[b, h, i * block:min(S, (i + 1) * block)] - exact))))
+    assert worst <= bound, (worst, bound)
+    assert worst > 0.0
+
+
+def test_fp8_full_sub_tile_is_64_keys():
+    # Keys 0..63 identical, keys 64..127 identical and scoring higher: inside each 64-key
+    # sub-tile all logits are equal, so every stored weight is exactly 1 (448) when it is
+    # formed, and the rescale is exact arithmetic. The result is then the exact softmax of
+    # the two logit levels over dequantised V. Sub-tiles of 128 keys would store the first
+    # half's weights as an E4M3 rounding of 2^(x_a - x_b) instead.
+    B, H, S, D, block = 1, 1, 128, 64, 128
+    q, _, v = gen.make_qkv(B, H, S, D, 45)
+    qf = f32(q)
+    kf = np.empty((B, H, S, D), np.float32)
+    kf[0, 0, :64] = 0.05 * qf[0, 0, 0]
+    kf[0, 0, 64:] = 0.2 * qf[0, 0, 0]
+    k = bf16(kf)
+    q8, qs = oracle.quantize_fp8(q, block)
+    k8, ks = oracle.quantize_fp8(k, block)
+    v8, vs = oracle.quantize_v_fp8(v)
+    out = oracle.attention_fp8_full(q8, qs, k8, ks, v8, vs, block, np.array([0, 1], np.int32),
+                                    np.array([0], np.int32), tokens=np.array([0]))
+    qhat = dequant(q8, qs[0, 0, 0].astype(np.float64))[0, 0, 0]
+    khat = dequant(k8, ks[0, 0, 0].astype(np.float64))[0, 0]
+    vhat = dequant(v8, vs[:, :, None, :].astype(np.float64))[0, 0]
+    x = khat @ qhat / math.sqrt(D)
+    xa, xb = x[0], x[64]
+    assert np.all(x[:64] == xa) and np.all(x[64:] == xb) and xb > xa + 0.5
+    w = np.exp(x - xb)
+    expect = (w @ vhat) / w.sum()
+    w_rounded = np.concatenate([e4m3_round(448 * np.exp2((xa - xb) * math.log2(math.e)))[None].repeat(64) / 448, np.ones(64)])
+    assert np.max(np.abs((w_rounded @ vhat) / w_rounded.sum() - expect)) > 1e-6  # the two readings differ here
+    assert np.max(np.abs(out[0] - expect)) <= 1e-12
