@@ -8,8 +8,9 @@ keep_ratio 0.15 (89 of 591 key blocks per query block).
 
 Prints one JSON line. `value` is milliseconds per step (lower is better). The line also
 carries the attention kernel's own time, its kept-block TFLOP/s against the bf16 MFMA
-peak (`roofline`), the fp8-QK variant, a dense (keep_ratio 1) forward for context, and
-the CPU oracle timed on a bounded sample on this host (`cpu_baseline`).
+peak (`roofline`), the fp8-QK variant, the full fp8 path (E4M3 Q, K, V and weights), a
+dense (keep_ratio 1) forward for context, and the CPU oracle timed on a bounded sample on
+this host (`cpu_baseline`).
 """
 import argparse
 import hashlib
@@ -246,6 +247,30 @@ def main():
     quant_ms = e[0].elapsed_time(e[1]) / reps
     fwd8_ms = e[1].elapsed_time(e[2]) / reps
 
+    # Full fp8 path: lists + Q/K codes from one pass, per-channel V codes, fp8 QK^T and PV.
+    rpf, cif, qf8, qfs, kf8, kfs = bsa.bsa_select_quantize(qd, kd, block, r, workspace=ws)
+    vt8, vts = bsa.bsa_quantize_v_fp8(vd, block)
+    outf = torch.empty_like(qd)
+    for _ in range(2):
+        bsa.bsa_forward_fp8_full(qf8, qfs, kf8, kfs, vt8, vts, block, rpf, cif, out=outf)
+    torch.cuda.synchronize()
+    ef = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ef[0].record()
+    for _ in range(reps):
+        bsa.bsa_select_quantize(qd, kd, block, r, workspace=ws, row_ptr=rpf, col_idx=cif)
+    ef[1].record()
+    for _ in range(reps):
+        bsa.bsa_quantize_v_fp8(vd, block, vt=vt8, scale=vts)
+    ef[2].record()
+    for _ in range(reps):
+        bsa.bsa_forward_fp8_full(qf8, qfs, kf8, kfs, vt8, vts, block, rpf, cif, out=outf)
+    ef[3].record()
+    torch.cuda.synchronize()
+    selq_ms = ef[0].elapsed_time(ef[1]) / reps
+    vq_ms = ef[1].elapsed_time(ef[2]) / reps
+    fwdf_ms = ef[2].elapsed_time(ef[3]) / reps
+    del rpf, cif, qf8, qfs, kf8, kfs, vt8, vts, outf
+
     dense = None
     if not args.no_dense:
         rp1 = torch.arange(rows + 1, dtype=torch.int32, device=dev) * n
@@ -306,6 +331,11 @@ def main():
         "fp8_qk": {"quantize_ms": round(quant_ms, 4), "attention_ms": round(fwd8_ms, 4),
                    "kept_tflops": round(flop / (fwd8_ms * 1e-3) / 1e12, 1),
                    "frac_mixed_peak": round(flop / (fwd8_ms * 1e-3) / 1e12 / (2 / (1 / FP8_PEAK_TFLOPS + 1 / BF16_PEAK_TFLOPS)), 4)},
+        "fp8_full": {"select_quantize_ms": round(selq_ms, 4), "quantize_v_ms": round(vq_ms, 4),
+                     "attention_ms": round(fwdf_ms, 4),
+                     "kept_tflops": round(flop / (fwdf_ms * 1e-3) / 1e12, 1),
+                     "frac_fp8_mfma_peak": round(flop / (fwdf_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                     "step_ms": round(selq_ms + vq_ms + fwdf_ms, 4)},
         "dense_keep_ratio_1": dense,
         "cpu_baseline": cpu,
     }

@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "BsaError", "lib_path", "bsa_num_blocks", "bsa_num_kept", "bsa_select_workspace_bytes",
     "bsa_pool", "bsa_select", "bsa_forward", "bsa_quantize_fp8", "bsa_forward_fp8",
-    "bsa_check_csr", "bsa_status_string", "bsa_last_error",
+    "bsa_check_csr", "bsa_status_string", "bsa_last_error", "bsa_vt_fp8_bytes", "bsa_select_quantize",
+    "bsa_quantize_v_fp8", "bsa_forward_fp8_full",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +57,10 @@ def _load():
         "bsa_check_csr": (ctypes.c_int, [P, P, i32, i32]),
         "bsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "bsa_last_error": (ctypes.c_char_p, []),
+        "bsa_vt_fp8_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "bsa_select_quantize": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, f64, P, P, P, P, P, P, P, sz, P]),
+        "bsa_quantize_v_fp8": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P]),
+        "bsa_forward_fp8_full": (ctypes.c_int, [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -197,6 +202,79 @@ def bsa_forward_fp8(q8, q_scale, k8, k_scale, v, block: int, row_ptr, col_idx, o
     _dev_tensor(out, "out", (torch.bfloat16,))
     _check(_load().bsa_forward_fp8(_p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(v), B, H, S, D, block,
                                    _p(row_ptr), _p(col_idx), _p(out), _stream(v)))
+    return out
+
+
+def bsa_vt_fp8_bytes(B, H, S, D, block) -> int:
+    return _load().bsa_vt_fp8_bytes(B, H, S, D, block)
+
+
+def bsa_select_quantize(q, k, block: int, keep_ratio: float, workspace=None, row_ptr=None, col_idx=None):
+    """(row_ptr, col_idx, q_codes, q_scale, k_codes, k_scale): bsa_select's lists and the
+    per-block E4M3 codes and scales of q and k, from one read of each block."""
+    _dev_tensor(q, "q", (torch.bfloat16,))
+    _dev_tensor(k, "k", (torch.bfloat16,))
+    if q.shape != k.shape:
+        raise ValueError("q and k shapes differ")
+    B, H, S, D = q.shape
+    n = bsa_num_blocks(S, block)
+    kept = bsa_num_kept(n, keep_ratio)
+    if kept == 0:
+        raise BsaError(1, "keep_ratio must be in (0, 1] (got %r)" % (keep_ratio,))
+    rows = B * H * n
+    if workspace is None:
+        workspace = torch.empty(max(bsa_select_workspace_bytes(B, H, S, D, block), 1), dtype=torch.uint8, device=q.device)
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
+    if col_idx is None:
+        col_idx = torch.empty(rows * kept, dtype=torch.int32, device=q.device)
+    q8 = torch.empty((B, H, S, D), dtype=torch.uint8, device=q.device)
+    k8 = torch.empty_like(q8)
+    qs = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    ks = torch.empty_like(qs)
+    _check(_load().bsa_select_quantize(_p(q), _p(k), B, H, S, D, block, keep_ratio, _p(row_ptr), _p(col_idx), _p(q8),
+                                       _p(qs), _p(k8), _p(ks), _p(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(q)))
+    return row_ptr, col_idx, q8, qs, k8, ks
+
+
+def bsa_quantize_v_fp8(v, block: int, vt=None, scale=None):
+    """(vt uint8 [B*H, D, ceil(S/block)*block] transposed, key-permuted E4M3 codes,
+    scale fp32 [B, H, D]) per (batch, head, channel)."""
+    _dev_tensor(v, "v", (torch.bfloat16,))
+    B, H, S, D = v.shape
+    n = bsa_num_blocks(S, block)
+    if vt is None:
+        vt = torch.empty((B * H, D, n * block), dtype=torch.uint8, device=v.device)
+    if scale is None:
+        scale = torch.empty((B, H, D), dtype=torch.float32, device=v.device)
+    if vt.numel() != bsa_vt_fp8_bytes(B, H, S, D, block):
+        raise ValueError("vt must hold bsa_vt_fp8_bytes bytes")
+    _check(_load().bsa_quantize_v_fp8(_p(v), B, H, S, D, block, _p(vt), _p(scale), _stream(v)))
+    return vt, scale
+
+
+def bsa_forward_fp8_full(q8, q_scale, k8, k_scale, vt8, v_scale, block: int, row_ptr, col_idx, out=None):
+    """Attention with E4M3 Q, K, V and E4M3 softmax weights; bf16 output [B, H, S, D]."""
+    _dev_tensor(q8, "q_e4m3", _ONE_BYTE)
+    _dev_tensor(k8, "k_e4m3", _ONE_BYTE)
+    _dev_tensor(vt8, "vt_e4m3", _ONE_BYTE, ndim=None)
+    if q8.shape != k8.shape:
+        raise ValueError("q_e4m3 and k_e4m3 shapes differ")
+    B, H, S, D = q8.shape
+    n = bsa_num_blocks(S, block)
+    if vt8.numel() != bsa_vt_fp8_bytes(B, H, S, D, block):
+        raise ValueError("vt_e4m3 must hold bsa_vt_fp8_bytes bytes for this shape and block")
+    for t, name, cnt in ((q_scale, "q_scale", B * H * n), (k_scale, "k_scale", B * H * n), (v_scale, "v_scale", B * H * D)):
+        _dev_tensor(t, name, (torch.float32,), ndim=None)
+        if t.numel() != cnt:
+            raise ValueError("%s must have %d entries" % (name, cnt))
+    _csr(row_ptr, col_idx, q8.device)
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=q8.device)
+    _dev_tensor(out, "out", (torch.bfloat16,))
+    _check(_load().bsa_forward_fp8_full(_p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(vt8), _p(v_scale), B, H, S, D,
+                                        block, _p(row_ptr), _p(col_idx), _p(out), _stream(q8)))
     return out
 
 

@@ -49,6 +49,9 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // is computed on a row's first sub-tile and almost never after it.
 constexpr float kSumLimit = 0x1p64f;
 
+// log2(448): 2^(x - m + log2 448) = 448 * 2^(x - m), the full fp8 path's weight scale.
+constexpr float kLog2Of448 = 8.807354922057604f;
+
 // 2^x on the transcendental unit (one v_exp_f32). Results below 2^-126 may flush to zero,
 // which is harmless for softmax weights.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -88,15 +91,22 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* base, int byte_off) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
 }
 
-template <int D, int BLK, bool FP8>
+// Attention modes: bf16 throughout; E4M3 Q/K with bf16 V; E4M3 Q/K, V and weights.
+constexpr int kModeBf16 = 0, kModeFp8QK = 1, kModeFp8Full = 2;
+
+template <int D, int BLK, int MODE>
 struct Cfg {
+    static constexpr bool FP8 = MODE != kModeBf16;     // Q and K as E4M3
+    static constexpr bool PV8 = MODE == kModeFp8Full;  // V (transposed, per channel) and P as E4M3
     static constexpr int NW = BLK / 32;                // waves per workgroup
     static constexpr int NT = NW * 64;                 // threads
-    static constexpr int VROWB = D * 2;                // V row bytes in LDS
+    // V tile in LDS: KT keys x D bf16 (row = key), or D channels x KT E4M3 codes (row = channel)
+    static constexpr int VROWB = PV8 ? KT : D * 2;     // V row bytes in LDS
+    static constexpr int VROWS = PV8 ? D : KT;
     static constexpr int KROWB = FP8 ? D : D * 2;      // K row bytes in LDS
     static constexpr int VCH = VROWB / 16;             // 16-byte chunks per V row
     static constexpr int KCH = KROWB / 16;
-    static constexpr int VTILE = KT * VROWB;
+    static constexpr int VTILE = VROWS * VROWB;
     static constexpr int KTILE = KT * KROWB;
     static constexpr int STAGE = KTILE + VTILE;
     static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;  // MFMA k-steps of S^T
@@ -120,10 +130,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-template <int D, int BLK, bool FP8>
+template <int D, int BLK, int MODE>
 __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_kernel(const AttnArgs a) {
-    using C = Cfg<D, BLK, FP8>;
+    using C = Cfg<D, BLK, MODE>;
+    constexpr bool FP8 = C::FP8, PV8 = C::PV8;
     static_assert(C::KSEGW >= 1 && C::VSEGW >= 1, "tile too small for the workgroup");
     __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE];
 
@@ -137,7 +148,10 @@ attn_kernel(const AttnArgs a) {
     const int bh = row / n, iq = row - bh * n;
     const int64_t bh_off = (int64_t)bh * S;  // token offset of this (b, h)
     const __amdgpu_buffer_rsrc_t krsrc = buffer_rsrc((const char*)a.k + bh_off * C::KROWB, (uint32_t)S * C::KROWB);
-    const __amdgpu_buffer_rsrc_t vrsrc = buffer_rsrc((const char*)a.v + bh_off * C::VROWB, (uint32_t)S * C::VROWB);
+    // V: bf16 rows of this (b, h), or its D channel rows of S_pad E4M3 codes
+    const __amdgpu_buffer_rsrc_t vrsrc =
+        PV8 ? buffer_rsrc((const char*)a.v + (int64_t)bh * D * a.S_pad, (uint32_t)D * a.S_pad)
+            : buffer_rsrc((const char*)a.v + bh_off * C::VROWB, (uint32_t)S * C::VROWB);
 
     // ---- Q operand (B of S^T = K Q^T), kept in registers --------------------------------
     const int q_tok = iq * BLK + wave * 32 + l32;
@@ -209,26 +223,34 @@ attn_kernel(const AttnArgs a) {
 #pragma unroll
     for (int x = 0; x < C::VSEGW; ++x) {
         const int r = (x * C::NW + wave) * C::VRPS + lane / C::VCH;
-        v_src[x] = r * C::VROWB + 16 * swz<C::VCH>(r, lane % C::VCH);
+        if constexpr (PV8)  // channel row r: 64 codes at r * S_pad in the buffer
+            v_src[x] = r * a.S_pad + 16 * ((lane % C::VCH) ^ ((r >> 2) & 3));
+        else
+            v_src[x] = r * C::VROWB + 16 * swz<C::VCH>(r, lane % C::VCH);
     }
     // Loads the sub-tile of nk keys (1 <= nk <= KT) starting at key0. Rows past the end of
-    // the sequence re-read its last row; their scores are masked.
+    // the sequence re-read its last row; their scores are masked. (The E4M3 V channel rows
+    // are zero padded to whole blocks and never need clamping.)
     auto issue_tile = [&](int key0, int nk, char* stage_base) {
-        const uint32_t ko = (uint32_t)key0 * C::KROWB, vo = (uint32_t)key0 * C::VROWB;
+        const uint32_t ko = (uint32_t)key0 * C::KROWB;
+        const uint32_t vo = PV8 ? (uint32_t)key0 : (uint32_t)key0 * C::VROWB;
+        const int last = nk - 1;
         if (nk == KT) {
 #pragma unroll
             for (int x = 0; x < C::KSEGW; ++x) dma16(krsrc, k_src[x], ko, stage_base + (x * C::NW + wave) * 1024);
-#pragma unroll
-            for (int x = 0; x < C::VSEGW; ++x)
-                dma16(vrsrc, v_src[x], vo, stage_base + C::KTILE + (x * C::NW + wave) * 1024);
         } else {
-            const int last = nk - 1;
 #pragma unroll
             for (int x = 0; x < C::KSEGW; ++x) {
                 const int r = (x * C::NW + wave) * C::KRPS + lane / C::KCH;
                 const int rr = r < last ? r : last;
                 dma16(krsrc, k_src[x] - (r - rr) * C::KROWB, ko, stage_base + (x * C::NW + wave) * 1024);
             }
+        }
+        if (PV8 || nk == KT) {
+#pragma unroll
+            for (int x = 0; x < C::VSEGW; ++x)
+                dma16(vrsrc, v_src[x], vo, stage_base + C::KTILE + (x * C::NW + wave) * 1024);
+        } else {
 #pragma unroll
             for (int x = 0; x < C::VSEGW; ++x) {
                 const int r = (x * C::NW + wave) * C::VRPS + lane / C::VCH;
@@ -248,13 +270,24 @@ attn_kernel(const AttnArgs a) {
     }
     const int gi = lane & 15;
     uint32_t v_rd1[D / 32], v_rd2[D / 32];
+    if constexpr (PV8) {
+        // A operand of the fp8 PV product: channel row l32 (+32 per ds), the 32 codes of this
+        // lane's key half (16-byte chunks 2h and 2h+1 of the row, swizzled by row bits 2..3)
 #pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-        const int dcol = 32 * ds + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
-        const int c = dcol >> 3, coff = (dcol & 7) * 2;
-        const int r1 = 4 * h + (gi >> 2), r2 = r1 + 8;
-        v_rd1[ds] = r1 * C::VROWB + 16 * swz<C::VCH>(r1, c) + coff;
-        v_rd2[ds] = r2 * C::VROWB + 16 * swz<C::VCH>(r2, c) + coff;
+        for (int ds = 0; ds < D / 32; ++ds) {
+            const int f = (l32 >> 2) & 3;
+            v_rd1[ds] = (32 * ds + l32) * C::VROWB + 16 * ((2 * h) ^ f);
+            v_rd2[ds] = (32 * ds + l32) * C::VROWB + 16 * ((2 * h + 1) ^ f);
+        }
+    } else {
+#pragma unroll
+        for (int ds = 0; ds < D / 32; ++ds) {
+            const int dcol = 32 * ds + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+            const int c = dcol >> 3, coff = (dcol & 7) * 2;
+            const int r1 = 4 * h + (gi >> 2), r2 = r1 + 8;
+            v_rd1[ds] = r1 * C::VROWB + 16 * swz<C::VCH>(r1, c) + coff;
+            v_rd2[ds] = r2 * C::VROWB + 16 * swz<C::VCH>(r2, c) + coff;
+        }
     }
 
     // ---- accumulators and softmax state (per lane: query column l32) -------------------
@@ -263,6 +296,12 @@ attn_kernel(const AttnArgs a) {
     for (int ds = 0; ds < D / 32; ++ds) o[ds] = (f32x16){};
     float m_used = -__builtin_inff();
     float lsum = 0.0f;
+    // Full fp8 path: the normaliser is the sum of the stored E4M3 weights, taken by one more
+    // MFMA whose A operand has a single row of ones (row 0; lanes 0 and 32): item 0 of lanes
+    // 0..31 accumulates sum_k P8[k][query].
+    f32x16 lacc = (f32x16){};
+    const int one_bits = (PV8 && l32 == 0) ? 0x38383838 : 0;  // E4M3 1.0 = 0x38
+    const i32x8 ones = {one_bits, one_bits, one_bits, one_bits, one_bits, one_bits, one_bits, one_bits};
 
     auto compute = [&](const char* kt, int nkeys, float tscale) __attribute__((always_inline)) {
         const char* vt = kt + C::KTILE;
@@ -301,6 +340,49 @@ attn_kernel(const AttnArgs a) {
                     int key = 32 * kh + 8 * (e >> 2) + 4 * h + (e & 3);
                     if (key >= nkeys) s[kh][e] = -__builtin_inff();
                 }
+        }
+
+        if constexpr (PV8) {
+            // Exact running maximum (the stored weights must stay <= 1), then the weights
+            // times 448 as E4M3 codes, in the byte order of the MFMA operand: byte e of this
+            // lane's 32 is key half kh = e / 16, accumulator item e % 16.
+            float mx = s[0][0];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
+            mx = pair_max(mx);
+            const float mt = mx * tscale;
+            if (__any(mt > m_used)) {
+                const float m_new = fmaxf(m_used, mt);
+                const float alpha = fast_exp2(m_used - m_new);  // 0 on a row's first sub-tile
+                m_used = m_new;
+                lacc[0] *= alpha;
+#pragma unroll
+                for (int ds = 0; ds < D / 32; ++ds) o[ds] *= alpha;
+            }
+            const float off = kLog2Of448 - m_used;
+            i32x8 p8;
+#pragma unroll
+            for (int wd = 0; wd < 8; ++wd) {
+                const int e = 4 * wd, kh = e >> 4, v = e & 15;
+                int w = 0;
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(fast_exp2(__builtin_fmaf(s[kh][v], tscale, off)),
+                                                    fast_exp2(__builtin_fmaf(s[kh][v + 1], tscale, off)), w, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(fast_exp2(__builtin_fmaf(s[kh][v + 2], tscale, off)),
+                                                    fast_exp2(__builtin_fmaf(s[kh][v + 3], tscale, off)), w, true);
+                p8[wd] = w;
+            }
+            lacc = mfma_fp8(ones, p8, lacc);
+#pragma unroll
+            for (int ds = 0; ds < D / 32; ++ds) {
+                const u32x4 lo = *(const u32x4*)(vt + v_rd1[ds]);
+                const u32x4 hi = *(const u32x4*)(vt + v_rd2[ds]);
+                const i32x8 vf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                o[ds] = mfma_fp8(vf, p8, o[ds]);
+            }
+            return;
         }
 
         // Online softmax in the log2 domain. The weights of each 16-key k-step are formed
@@ -435,7 +517,15 @@ attn_kernel(const AttnArgs a) {
     }
 
     // ---- normalise and write --------------------------------------------------------
-    const float ltot = pair_sum(lsum);
+    float ltot;
+    if constexpr (PV8) {
+        // lanes 0..31 hold the sum of the stored codes (448 x weights); lanes 32..63 take it
+        // from their partner
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lacc[0]), __float_as_uint(lacc[0]), false, false);
+        ltot = h ? __uint_as_float(sw[0]) : lacc[0];
+    } else {
+        ltot = pair_sum(lsum);
+    }
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     if (q_tok < S) {
         __bf16* op = (__bf16*)a.out + (bh_off + q_tok) * D + 4 * h;
@@ -443,9 +533,11 @@ attn_kernel(const AttnArgs a) {
         for (int ds = 0; ds < D / 32; ++ds)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
+                f32x4 vs = {1.0f, 1.0f, 1.0f, 1.0f};
+                if constexpr (PV8) vs = *(const f32x4*)(a.v_scale + (int64_t)bh * D + 32 * ds + 8 * g + 4 * h);
                 bf16x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[ds][4 * g + e] * inv);
+                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[ds][4 * g + e] * vs[e] * inv);
                 *(bf16x4*)(op + 32 * ds + 8 * g) = w;
             }
     }
@@ -453,18 +545,25 @@ attn_kernel(const AttnArgs a) {
 
 }  // namespace
 
-template <int D, int BLK, bool FP8>
+template <int D, int BLK, int MODE>
 static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     const int grid = a.BH * a.n;
-    hipLaunchKernelGGL((attn_kernel<D, BLK, FP8>), dim3(grid), dim3(BLK * 2), 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<D, BLK, MODE>), dim3(grid), dim3(BLK * 2), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, int D, int block, bool fp8, hipStream_t stream) {
-    if (D == 128 && block == 128) return fp8 ? launch<128, 128, true>(a, stream) : launch<128, 128, false>(a, stream);
-    if (D == 128 && block == 64) return fp8 ? launch<128, 64, true>(a, stream) : launch<128, 64, false>(a, stream);
-    if (D == 64 && block == 128) return fp8 ? launch<64, 128, true>(a, stream) : launch<64, 128, false>(a, stream);
-    if (D == 64 && block == 64) return fp8 ? launch<64, 64, true>(a, stream) : launch<64, 64, false>(a, stream);
+template <int D, int BLK>
+static hipError_t launch_mode(const AttnArgs& a, int mode, hipStream_t stream) {
+    if (mode == kModeFp8Full) return launch<D, BLK, kModeFp8Full>(a, stream);
+    if (mode == kModeFp8QK) return launch<D, BLK, kModeFp8QK>(a, stream);
+    return launch<D, BLK, kModeBf16>(a, stream);
+}
+
+hipError_t launch_attention(const AttnArgs& a, int D, int block, int mode, hipStream_t stream) {
+    if (D == 128 && block == 128) return launch_mode<128, 128>(a, mode, stream);
+    if (D == 128 && block == 64) return launch_mode<128, 64>(a, mode, stream);
+    if (D == 64 && block == 128) return launch_mode<64, 128>(a, mode, stream);
+    if (D == 64 && block == 64) return launch_mode<64, 64>(a, mode, stream);
     return hipErrorInvalidValue;
 }
 

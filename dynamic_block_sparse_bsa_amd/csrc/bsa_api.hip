@@ -39,6 +39,9 @@ bsa_status check_shape(int32_t B, int32_t H, int32_t S, int32_t D, int32_t block
     if (elems >= ((int64_t)1 << 40)) return fail(BSA_ERR_UNSUPPORTED, "tensor too large");
     const int64_t rows = (int64_t)B * H * ((S + block - 1) / block);
     if (rows >= ((int64_t)1 << 31)) return fail(BSA_ERR_UNSUPPORTED, "too many block rows");
+    // one (b, h) slice is addressed through a buffer resource with 32-bit offsets
+    const int64_t s_pad = (int64_t)((S + block - 1) / block) * block;
+    if (s_pad * D * 2 >= ((int64_t)1 << 31)) return fail(BSA_ERR_UNSUPPORTED, "sequence too long for one (b, h) slice (S = %d)", S);
     return BSA_OK;
 }
 
@@ -141,13 +144,16 @@ bsa_status bsa_select(const void* q, const void* k, int32_t B, int32_t H, int32_
     return hip_result(bsa::launch_select(qbar, kbarT, B * H, n, D, kept, row_ptr, col_idx, s), "select launch");
 }
 
+// mode: 0 = bf16, 1 = E4M3 Q/K with bf16 V, 2 = E4M3 Q/K, V (transposed) and weights.
 static bsa_status forward_common(const void* q, const float* q_scale, const void* k, const float* k_scale, const void* v,
-                                 int32_t B, int32_t H, int32_t S, int32_t D, int32_t block, const int32_t* row_ptr,
-                                 const int32_t* col_idx, void* out, void* hip_stream, bool fp8) {
+                                 const float* v_scale, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                                 const int32_t* row_ptr, const int32_t* col_idx, void* out, void* hip_stream, int mode) {
     bsa_status st = check_shape(B, H, S, D, block);
     if (st != BSA_OK) return st;
     if (!q || !k || !v || !row_ptr || !col_idx || !out) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
-    if (fp8 && (!q_scale || !k_scale)) return fail(BSA_ERR_INVALID_ARGUMENT, "null scale pointer");
+    if (mode != 0 && (!q_scale || !k_scale)) return fail(BSA_ERR_INVALID_ARGUMENT, "null scale pointer");
+    if (mode == 2 && (!v_scale || ((uintptr_t)v_scale & 15u)))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "v_scale must be non-null and 16-byte aligned");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
     if (((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u)) return fail(BSA_ERR_INVALID_ARGUMENT, "misaligned CSR arrays");
@@ -159,26 +165,81 @@ static bsa_status forward_common(const void* q, const float* q_scale, const void
     a.v = v;
     a.q_scale = q_scale;
     a.k_scale = k_scale;
+    a.v_scale = v_scale;
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
     a.out = out;
     a.BH = B * H;
     a.S = S;
     a.n = bsa_num_blocks(S, block);
+    a.S_pad = a.n * block;
     a.sm_scale_log2 = (float)(kLog2e / sqrt((double)D));
-    return hip_result(bsa::launch_attention(a, D, block, fp8, as_stream(hip_stream)), "attention launch");
+    return hip_result(bsa::launch_attention(a, D, block, mode, as_stream(hip_stream)), "attention launch");
 }
 
 bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t B, int32_t H, int32_t S, int32_t D,
                        int32_t block, const int32_t* row_ptr, const int32_t* col_idx, void* out, void* hip_stream) {
-    return forward_common(q, nullptr, k, nullptr, v, B, H, S, D, block, row_ptr, col_idx, out, hip_stream, false);
+    return forward_common(q, nullptr, k, nullptr, v, nullptr, B, H, S, D, block, row_ptr, col_idx, out, hip_stream, 0);
 }
 
 bsa_status bsa_forward_fp8(const void* q_e4m3, const float* q_scale, const void* k_e4m3, const float* k_scale,
                            const void* v, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
                            const int32_t* row_ptr, const int32_t* col_idx, void* out, void* hip_stream) {
-    return forward_common(q_e4m3, q_scale, k_e4m3, k_scale, v, B, H, S, D, block, row_ptr, col_idx, out, hip_stream,
-                          true);
+    return forward_common(q_e4m3, q_scale, k_e4m3, k_scale, v, nullptr, B, H, S, D, block, row_ptr, col_idx, out,
+                          hip_stream, 1);
+}
+
+size_t bsa_vt_fp8_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t block) {
+    if (B < 1 || H < 1 || S < 1 || D < 1 || block < 1) return 0;
+    return (size_t)B * H * D * (size_t)bsa_num_blocks(S, block) * block;
+}
+
+bsa_status bsa_select_quantize(const void* q, const void* k, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                               double keep_ratio, int32_t* row_ptr, int32_t* col_idx, void* q_e4m3, float* q_scale,
+                               void* k_e4m3, float* k_scale, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    bsa_status st = check_shape(B, H, S, D, block);
+    if (st != BSA_OK) return st;
+    if (!q || !k || !row_ptr || !col_idx || !workspace || !q_e4m3 || !q_scale || !k_e4m3 || !k_scale)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(workspace) || !aligned16(q_e4m3) || !aligned16(k_e4m3))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, the code buffers and workspace must be 16-byte aligned");
+    if (((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u) || ((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "misaligned CSR or scale arrays");
+    const int32_t n = bsa_num_blocks(S, block);
+    const int32_t kept = bsa_num_kept(n, keep_ratio);
+    if (kept == 0) return fail(BSA_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1] (got %g)", keep_ratio);
+    if (n > bsa::kMaxSelectBlocks) return fail(BSA_ERR_UNSUPPORTED, "bsa_select_quantize supports at most %d blocks per sequence (got %d)", bsa::kMaxSelectBlocks, n);
+    if ((int64_t)B * H * n * kept >= ((int64_t)1 << 31)) return fail(BSA_ERR_UNSUPPORTED, "kept-block list too long for int32 indices");
+    const size_t need = bsa_select_workspace_bytes(B, H, S, D, block);
+    if (workspace_bytes < need) return fail(BSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    if ((st = check_device()) != BSA_OK) return st;
+    float* qbar = (float*)workspace;
+    float* kbarT = qbar + (size_t)B * H * n * D;
+    hipStream_t s = as_stream(hip_stream);
+    if ((st = hip_result(bsa::launch_pool_quant_qk(q, k, B * H, S, D, block, qbar, kbarT, q_e4m3, k_e4m3, q_scale, k_scale, s),
+                         "pool/quantise launch")) != BSA_OK)
+        return st;
+    return hip_result(bsa::launch_select(qbar, kbarT, B * H, n, D, kept, row_ptr, col_idx, s), "select launch");
+}
+
+bsa_status bsa_quantize_v_fp8(const void* v, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block, void* vt_e4m3,
+                              float* v_scale, void* hip_stream) {
+    bsa_status st = check_shape(B, H, S, D, block);
+    if (st != BSA_OK) return st;
+    if (!v || !vt_e4m3 || !v_scale) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(v) || !aligned16(vt_e4m3) || !aligned16(v_scale))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "v, vt_e4m3 and v_scale must be 16-byte aligned");
+    if ((st = check_device()) != BSA_OK) return st;
+    return hip_result(bsa::launch_quantize_v(v, B * H, S, D, block, vt_e4m3, v_scale, as_stream(hip_stream)),
+                      "quantise V launch");
+}
+
+bsa_status bsa_forward_fp8_full(const void* q_e4m3, const float* q_scale, const void* k_e4m3, const float* k_scale,
+                                const void* vt_e4m3, const float* v_scale, int32_t B, int32_t H, int32_t S, int32_t D,
+                                int32_t block, const int32_t* row_ptr, const int32_t* col_idx, void* out,
+                                void* hip_stream) {
+    return forward_common(q_e4m3, q_scale, k_e4m3, k_scale, vt_e4m3, v_scale, B, H, S, D, block, row_ptr, col_idx, out,
+                          hip_stream, 2);
 }
 
 bsa_status bsa_quantize_fp8(const void* x, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block, void* x_e4m3,

@@ -8,17 +8,28 @@ namespace bsa {
 struct AttnArgs {
     const void* q;          // bf16 or E4M3 [B,H,S,D]
     const void* k;          // bf16 or E4M3 [B,H,S,D]
-    const void* v;          // bf16 [B,H,S,D]
+    const void* v;          // bf16 [B,H,S,D], or (full fp8 path) E4M3 [B*H, D, S_pad], key-permuted
     const float* q_scale;   // [B*H*n] (fp8 only)
     const float* k_scale;   // [B*H*n] (fp8 only)
+    const float* v_scale;   // [B*H*D] (full fp8 path only)
     const int32_t* row_ptr;
     const int32_t* col_idx;
     void* out;              // bf16 [B,H,S,D]
     int BH, S, n;
+    int S_pad;              // n * block (full fp8 path only)
     float sm_scale_log2;    // log2(e) / sqrt(D)
 };
 
-hipError_t launch_attention(const AttnArgs& a, int D, int block, bool fp8, hipStream_t stream);
+// mode: 0 = bf16, 1 = E4M3 Q/K with bf16 V, 2 = E4M3 Q/K, V and weights.
+hipError_t launch_attention(const AttnArgs& a, int D, int block, int mode, hipStream_t stream);
+
+// Block means of Q (row-major) and K (transposed) and their per-block E4M3 codes and scales,
+// from one read of each block.
+hipError_t launch_pool_quant_qk(const void* q, const void* k, int BH, int S, int D, int block, float* qbar, float* kbarT,
+                                void* q8, void* k8, float* qscale, float* kscale, hipStream_t stream);
+
+// Per-channel E4M3 codes of V, transposed and key-permuted ([BH, D, n*block]), and scales.
+hipError_t launch_quantize_v(const void* v, int BH, int S, int D, int block, void* vt, float* vscale, hipStream_t stream);
 
 // Block means of x (bf16 [BH,S,D]) into fp32: row-major [BH,n,D], or [BH,D,n] if transposed.
 hipError_t launch_pool(const void* x, int BH, int S, int D, int block, float* xbar, bool transposed,

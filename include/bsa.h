@@ -15,7 +15,9 @@
  *
  * The calls follow that split: bsa_select() estimates importance from block means and
  * returns the kept key-block lists; bsa_forward() computes attention over only those
- * blocks. bsa_quantize_fp8() and bsa_forward_fp8() are the FP8 path.
+ * blocks. bsa_quantize_fp8() and bsa_forward_fp8() are the FP8 path (E4M3 Q and K);
+ * bsa_select_quantize(), bsa_quantize_v_fp8() and bsa_forward_fp8_full() are the full FP8
+ * path (E4M3 Q, K, V and softmax weights).
  *
  * Conventions shared by every call:
  *   - Tensors are contiguous [B, H, S, D] row-major (D fastest); q, k, v and out hold
@@ -25,7 +27,8 @@
  *     n = ceil(S/block) blocks, the last possibly partial. Query and key blocks are the
  *     same partition.
  *   - Supported: D in {64, 128}; block in {64, 128}; S >= 1; B, H >= 1; B*H*S*D < 2^40;
- *     n <= 8192 for bsa_select. Other shapes return BSA_ERR_UNSUPPORTED.
+ *     ceil(S/block)*block*D*2 < 2^31 (one (b, h) slice); n <= 8192 for bsa_select and
+ *     bsa_select_quantize. Other shapes return BSA_ERR_UNSUPPORTED.
  *   - Kept-block lists are CSR over the B*H*n query-block rows, row r = (b*H + h)*n + i:
  *     row_ptr int32 [B*H*n + 1], col_idx int32 [row_ptr[B*H*n]]; each row's key-block
  *     indices are strictly ascending in [0, n).
@@ -126,6 +129,56 @@ bsa_status bsa_forward_fp8(const void* q_e4m3, const float* q_scale, const void*
                            const float* k_scale, const void* v, int32_t B, int32_t H, int32_t S,
                            int32_t D, int32_t block, const int32_t* row_ptr,
                            const int32_t* col_idx, void* out, void* hip_stream);
+
+/* ---- Full FP8 path --------------------------------------------------------------------
+ * Source: the same pages, section 动态稀疏量化注意力 / step 3: the sparse path joined with
+ * SageAttention2 into an FP8 attention path. The pages give none of its steps; this is
+ * the library's reading of them:
+ *   - Q and K: OCP E4M3FN per (b*h, token block), scale = absmax/448 in fp32 (1 for an
+ *     all-zero block), code = nearest E4M3 (ties to even) to x/scale in fp32; the same
+ *     codes and scales as bsa_quantize_fp8.
+ *   - V: E4M3FN per (b*h, channel d) over the whole sequence, same scale and rounding rule.
+ *   - Softmax: online over the kept keys in list order, 64 keys at a time; after a 64-key
+ *     sub-tile raises the running maximum m of the log2-domain logits x, its weights
+ *     2^(x - m) <= 1 are stored as E4M3 codes of 448 * weight; the output is the sum of
+ *     stored weight x dequantised V divided by the sum of the stored weights, in bf16.
+ */
+
+/* Bytes of the transposed V codes for bsa_quantize_v_fp8: B*H*D*ceil(S/block)*block; 0 on
+ * bad input. */
+size_t bsa_vt_fp8_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t block);
+
+/* bsa_select (same lists, bit for bit) and, from the same single read of every Q and K
+ * block, their E4M3 codes and per-block scales (the bytes bsa_quantize_fp8 writes).
+ *   q_e4m3, k_e4m3: uint8 [B, H, S, D] (16-byte aligned); q_scale, k_scale: fp32 [B*H*n].
+ *   workspace: as for bsa_select (bsa_select_workspace_bytes). */
+bsa_status bsa_select_quantize(const void* q, const void* k, int32_t B, int32_t H, int32_t S,
+                               int32_t D, int32_t block, double keep_ratio, int32_t* row_ptr,
+                               int32_t* col_idx, void* q_e4m3, float* q_scale, void* k_e4m3,
+                               float* k_scale, void* workspace, size_t workspace_bytes,
+                               void* hip_stream);
+
+/* V (bf16 [B, H, S, D]) to per-channel E4M3 codes and scales.
+ *   vt_e4m3: uint8 [B*H, D, S_pad] with S_pad = ceil(S/block)*block (bsa_vt_fp8_bytes);
+ *     row (b*h, d) holds the codes of channel d over the sequence, zero past S, and inside
+ *     every group of 64 keys key r = 32*kh + 8*(v/4) + 4*g + v%4 (kh, g in {0,1}, v < 16)
+ *     sits at position 32*g + 16*kh + v. This layout is the operand order of the attention
+ *     kernel; it is only meant as the input of bsa_forward_fp8_full with the same block.
+ *   v_scale: fp32 [B*H, D], 16-byte aligned; used as scratch (channel maxima) until the
+ *     call's last kernel writes the scales.
+ *   The call runs four kernels on hip_stream (clear, channel maxima, codes, scales). */
+bsa_status bsa_quantize_v_fp8(const void* v, int32_t B, int32_t H, int32_t S, int32_t D,
+                              int32_t block, void* vt_e4m3, float* v_scale, void* hip_stream);
+
+/* Attention over the kept blocks with E4M3 Q, K (from bsa_select_quantize or
+ * bsa_quantize_fp8), V (from bsa_quantize_v_fp8 with the same block) and E4M3 softmax
+ * weights as described above; both products run on fp8 MFMA with fp32 accumulation; out
+ * is bf16 [B, H, S, D]. Same CSR rules as bsa_forward. */
+bsa_status bsa_forward_fp8_full(const void* q_e4m3, const float* q_scale, const void* k_e4m3,
+                                const float* k_scale, const void* vt_e4m3, const float* v_scale,
+                                int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                                const int32_t* row_ptr, const int32_t* col_idx, void* out,
+                                void* hip_stream);
 
 /* Host-side validator for a CSR held in host memory: row_ptr[0] == 0, non-decreasing,
  * every row's indices strictly ascending in [0, n_blocks). Returns BSA_OK or

@@ -6,7 +6,9 @@ Criteria (all compare against the CPU oracle in fp64):
       ascending in-range indices and every selected score must be >= every unselected
       score - 1e-4 (oracle scores);
   bf16 attention   -- max abs error <= 2e-2 and mean abs error <= 2e-3;
-  fp8-QK attention -- max abs error <= 6e-2 against the unquantised oracle.
+  fp8-QK attention -- max abs error <= 6e-2 against the unquantised oracle;
+  full fp8 attention -- against the oracle's full-fp8 attention: mean <= 2e-3, max <= 6e-2,
+      and at most 1 % of the query rows beyond 2e-2 (see check_fp8_full).
 """
 import numpy as np
 import torch
@@ -14,6 +16,15 @@ import torch
 GAP = 1e-4
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
 FP8_MAX = 6e-2
+# Full fp8 path against the oracle that rounds its weights the same way. The two sides
+# differ only in fp32 vs fp64 arithmetic, but a weight whose 448 * p lies within that
+# difference of an E4M3 midpoint can round one code apart (a relative step of at most 2^-3);
+# the flip moves that query's output by at most 2^-3 * (the key's share of the row weight)
+# * 2 max|v| -- on every element of that query's row. The bulk must still agree to the bf16
+# bar: at most FP8_FULL_OUTLIER_ROWS of the query rows may exceed BF16_MAX anywhere, no
+# element FP8_FULL_MAX, and the mean stays at BF16_MEAN.
+FP8_FULL_MAX = 6e-2
+FP8_FULL_OUTLIER_ROWS = 1e-2
 
 
 def to_dev(bits, device="cuda:0"):
@@ -50,3 +61,13 @@ def check_lists(gpu_row_ptr, gpu_col, ref):
 def errors(got, expect):
     e = np.abs(np.asarray(got, dtype=np.float64) - expect)
     return float(e.max()), float(e.mean())
+
+
+def check_fp8_full(got, expect):
+    """Full fp8 path criteria (see FP8_FULL_MAX) over outputs whose last axis is D; returns
+    (max, mean, fraction of query rows beyond the bf16 bar)."""
+    err = np.abs(np.asarray(got, np.float64) - np.asarray(expect, np.float64))
+    mx, mean = float(err.max()), float(err.mean())
+    frac = float(np.mean(err.max(axis=-1) > BF16_MAX))
+    assert mx <= FP8_FULL_MAX and mean <= BF16_MEAN and frac <= FP8_FULL_OUTLIER_ROWS, (mx, mean, frac)
+    return mx, mean, frac

@@ -15,7 +15,7 @@ import torch
 import dynamic_block_sparse_bsa_amd as bsa
 import gen
 import oracle
-from parity import BF16_MAX, BF16_MEAN, FP8_MAX, check_lists, errors, to_dev, to_f64
+from parity import BF16_MAX, BF16_MEAN, FP8_MAX, check_fp8_full, check_lists, errors, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -91,3 +91,50 @@ def test_full_size_fp8():
     mx8, mean8 = errors(got, expect8)
     print("fp8 vs oracle on the same E4M3 operands: max %.3e mean %.3e" % (mx8, mean8))
     assert mx8 <= BF16_MAX and mean8 <= BF16_MEAN
+
+
+def natural_from_vt(vt, B, H, S, D, block):
+    """Undo bsa_quantize_v_fp8's transposed, key-permuted layout (defined in include/bsa.h)."""
+    n = oracle.num_blocks(S, block)
+    S_pad = n * block
+    pos = np.arange(64)
+    g, e = pos // 32, pos % 32
+    key = 32 * (e // 16) + 8 * ((e % 16) // 4) + 4 * g + (e % 16) % 4
+    order = np.empty(S_pad, np.int64)
+    for grp in range(S_pad // 64):
+        order[64 * grp + key] = 64 * grp + pos
+    nat = np.asarray(vt).reshape(B * H, D, S_pad)[:, :, order]
+    return nat[:, :, :S].transpose(0, 2, 1).reshape(B, H, S, D), nat[:, :, S:]
+
+
+def test_full_size_fp8_full():
+    """The full fp8 path (E4M3 Q, K, V and weights) at the 720p fp8 workload."""
+    q, k, v, cfg, ref = workload("fp8")
+    B, H, S, D, block = q.shape + (cfg["block"],)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    rp, ci, q8, qs, k8, ks = bsa.bsa_select_quantize(qd, kd, block, cfg["keep_ratio"])
+    check_lists(rp.cpu().numpy(), ci.cpu().numpy(), ref)
+    oq8, oqs = oracle.quantize_fp8(q, block)
+    ok8, oks = oracle.quantize_fp8(k, block)
+    assert np.array_equal(qs.cpu().numpy(), oqs) and np.array_equal(ks.cpu().numpy(), oks)
+    assert np.array_equal(q8.cpu().numpy(), oq8) and np.array_equal(k8.cpu().numpy(), ok8)
+    del oq8, ok8
+    vt, vs = bsa.bsa_quantize_v_fp8(vd, block)
+    ov8, ovs = oracle.quantize_v_fp8(v)
+    codes, pad = natural_from_vt(vt.cpu().numpy(), B, H, S, D, block)
+    assert np.array_equal(codes, ov8) and np.all(pad == 0)
+    assert np.array_equal(vs.cpu().numpy(), ovs)
+    del codes, pad
+    gc.collect()
+    out = bsa.bsa_forward_fp8_full(q8, qs, k8, ks, vt, vs, block, rp, ci)
+    tok = sample_tokens(B, H, S, seed=2)
+    got = rows_of(out, tok, D)
+    grp, gci = rp.cpu().numpy(), ci.cpu().numpy()
+    oq8, oqs = oracle.quantize_fp8(q, block)
+    ok8, oks = oracle.quantize_fp8(k, block)
+    expect = oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, grp, gci, tokens=tok)
+    mx, mean, frac = check_fp8_full(got, expect)
+    print("fp8 full vs oracle: max %.3e mean %.3e rows beyond bf16 bar %.4f" % (mx, mean, frac))
+    exact = oracle.attention(q, k, v, block, grp, gci, tokens=tok)
+    mx2, mean2 = errors(got, exact)
+    print("fp8 full vs unquantised attention (reported): max %.3e mean %.3e" % (mx2, mean2))

@@ -14,7 +14,7 @@ import torch
 import dynamic_block_sparse_bsa_amd as bsa
 import gen
 import oracle
-from parity import BF16_MAX, BF16_MEAN, FP8_MAX, check_lists, errors, to_dev, to_f64
+from parity import BF16_MAX, BF16_MEAN, FP8_MAX, check_fp8_full, check_lists, errors, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -226,3 +226,96 @@ def test_keep_ratio_sweep():
         assert mx <= BF16_MAX and mean <= BF16_MEAN, (r, mx, mean)
         dist.append(float(np.mean(np.abs(out - dense))))
     assert dist[-1] <= dist[0], dist
+
+
+# ---- full FP8 path ---------------------------------------------------------------------
+
+def natural_from_vt(vt, B, H, S, D, block):
+    """Undo the transposed, key-permuted layout of bsa_quantize_v_fp8 (defined in
+    include/bsa.h: key r = 32*kh + 8*(v/4) + 4*g + v%4 of a 64-key group sits at position
+    32*g + 16*kh + v) into [B, H, S, D] codes, and return the padding columns too."""
+    n = oracle.num_blocks(S, block)
+    S_pad = n * block
+    vt = np.asarray(vt).reshape(B * H, D, S_pad)
+    pos = np.arange(64)
+    g, e = pos // 32, pos % 32
+    kh, v = e // 16, e % 16
+    key = 32 * kh + 8 * (v // 4) + 4 * g + v % 4
+    order = np.empty(S_pad, np.int64)
+    for grp in range(S_pad // 64):
+        order[64 * grp + key] = 64 * grp + pos  # natural key -> stored position
+    nat = vt[:, :, order]  # [B*H, D, S_pad] in natural key order
+    return nat[:, :, :S].transpose(0, 2, 1).reshape(B, H, S, D), nat[:, :, S:]
+
+
+FP8_FULL_CASES = [c for c in SMALL if c[5] < 1.0 or c[2] < 300]
+
+
+@pytest.mark.parametrize("case", FP8_FULL_CASES, ids=lambda c: "B%dH%dS%dD%db%dr%g" % c[:6])
+def test_select_quantize(case):
+    B, H, S, D, block, r = case[:6]
+    q, k, v, qd, kd, vd = run_small(*case)
+    rp, ci = bsa.bsa_select(qd, kd, block, r)
+    rp2, ci2, q8, qs, k8, ks = bsa.bsa_select_quantize(qd, kd, block, r)
+    assert torch.equal(rp, rp2) and torch.equal(ci, ci2)
+    oq8, oqs = oracle.quantize_fp8(q, block)
+    ok8, oks = oracle.quantize_fp8(k, block)
+    assert np.array_equal(q8.cpu().numpy(), oq8) and np.array_equal(k8.cpu().numpy(), ok8)
+    assert np.array_equal(qs.cpu().numpy(), oqs) and np.array_equal(ks.cpu().numpy(), oks)
+
+
+@pytest.mark.parametrize("case", FP8_FULL_CASES, ids=lambda c: "B%dH%dS%dD%db%dr%g" % c[:6])
+def test_quantize_v_fp8(case):
+    B, H, S, D, block = case[:5]
+    q, k, v, qd, kd, vd = run_small(*case)
+    vt, vs = bsa.bsa_quantize_v_fp8(vd, block)
+    codes, pad = natural_from_vt(vt.cpu().numpy(), B, H, S, D, block)
+    ov8, ovs = oracle.quantize_v_fp8(v)
+    assert np.array_equal(codes, ov8)
+    assert np.all(pad == 0)
+    assert np.array_equal(vs.cpu().numpy(), ovs)
+
+
+@pytest.mark.parametrize("case", FP8_FULL_CASES, ids=lambda c: "B%dH%dS%dD%db%dr%g" % c[:6])
+def test_fp8_full_forward(case):
+    B, H, S, D, block, r = case[:6]
+    q, k, v, qd, kd, vd = run_small(*case)
+    rp, ci, q8, qs, k8, ks = bsa.bsa_select_quantize(qd, kd, block, r)
+    vt, vs = bsa.bsa_quantize_v_fp8(vd, block)
+    ref = oracle.select(q, k, block, r)
+    orp, oci = torch.from_numpy(ref["row_ptr"]).cuda(), torch.from_numpy(ref["col_idx"]).cuda()
+    out = to_f64(bsa.bsa_forward_fp8_full(q8, qs, k8, ks, vt, vs, block, orp, oci))
+    oq8, oqs = oracle.quantize_fp8(q, block)
+    ok8, oks = oracle.quantize_fp8(k, block)
+    ov8, ovs = oracle.quantize_v_fp8(v)
+    expect = oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, ref["row_ptr"], ref["col_idx"])
+    check_fp8_full(out, expect)
+
+
+def test_fp8_full_forward_rising_scores_and_ragged_lists():
+    """Row maxima that move mid-row, lists of mixed length with empty rows (full fp8 path)."""
+    B, H, S, D, block = 1, 2, 6 * 128 - 40, 128, 128
+    q, k, v = gen.make_qkv(B, H, S, D, 35)
+    kk = gen.bf16_bits_to_f32(k).astype(np.float64)
+    n = oracle.num_blocks(S, block)
+    for j in range(n):
+        kk[:, :, j * block:(j + 1) * block, :] *= 1.0 + 0.7 * j
+    k = gen.f32_to_bf16_bits(kk.astype(np.float32))
+    rows = B * H * n
+    rng = np.random.default_rng(6)
+    lens = rng.integers(0, n + 1, size=rows)
+    lens[1] = 0
+    lists = [np.sort(rng.choice(n, size=L, replace=False)).astype(np.int32) for L in lens]
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ci = np.concatenate(lists).astype(np.int32)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    _, _, q8, qs, k8, ks = bsa.bsa_select_quantize(qd, kd, block, 0.5)
+    vt, vs = bsa.bsa_quantize_v_fp8(vd, block)
+    out = to_f64(bsa.bsa_forward_fp8_full(q8, qs, k8, ks, vt, vs, block, torch.from_numpy(rp).cuda(),
+                                          torch.from_numpy(ci).cuda()))
+    oq8, oqs = oracle.quantize_fp8(q, block)
+    ok8, oks = oracle.quantize_fp8(k, block)
+    ov8, ovs = oracle.quantize_v_fp8(v)
+    expect = oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, rp, ci)
+    check_fp8_full(out, expect)
+    assert np.all(out[0, 0, block:2 * block] == 0.0)  # row 1 has an empty list
