@@ -139,3 +139,27 @@ def test_binding_requires_device_tensors():
     x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         bsa.bsa_forward(x, x, x, 64, torch.zeros(2, dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
+
+
+def test_full_fp8_calls_check_arguments_on_the_host():
+    A = ctypes.c_void_p
+    # bytes of the transposed V codes: B*H*D*ceil(S/block)*block
+    assert bsa.bsa_vt_fp8_bytes(1, 40, 75600, 128, 128) == 40 * 128 * 591 * 128
+    assert bsa.bsa_vt_fp8_bytes(2, 3, 1, 64, 64) == 2 * 3 * 64 * 64
+    assert bsa.bsa_vt_fp8_bytes(0, 1, 1, 64, 64) == 0
+    # null v_scale / misaligned v_scale for the full fp8 forward
+    st = lib().bsa_forward_fp8_full(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 128, 128, 128, FAKE, FAKE, A(0x50000), None)
+    assert st == 1, bsa.bsa_last_error()
+    st = lib().bsa_forward_fp8_full(FAKE, FAKE, FAKE, FAKE, FAKE, A(0x60004), 1, 1, 128, 128, 128, FAKE, FAKE, A(0x50000), None)
+    assert st == 1
+    # unsupported shapes and a one-(b, h) slice too long for 32-bit buffer offsets
+    st = lib().bsa_quantize_v_fp8(FAKE, 1, 1, 128, 96, 128, FAKE, FAKE, None)
+    assert st == 2
+    st = lib().bsa_quantize_v_fp8(FAKE, 1, 1, 1 << 23, 128, 128, FAKE, FAKE, None)
+    assert st == 2, bsa.bsa_last_error()
+    # select_quantize: keep_ratio and workspace checked before any device work
+    st = lib().bsa_select_quantize(FAKE, FAKE, 1, 1, 1024, 64, 64, 0.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 20, None)
+    assert st == 1
+    st = lib().bsa_select_quantize(FAKE, FAKE, 1, 1, 1024, 64, 64, 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == 3
