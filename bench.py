@@ -152,6 +152,101 @@ def sweep(args):
         torch.cuda.empty_cache()
 
 
+def sample_power(stop, samples):
+    """Append (time, socket watts, GFX clock MHz) from amd-smi about once a second until stop is set."""
+    import re
+    import subprocess
+
+    while not stop.is_set():
+        t = time.time()
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=10).stdout
+        except (OSError, subprocess.TimeoutExpired):
+            return
+        pw = re.search(r"SOCKET_POWER:\s*(\d+)", r)
+        ck = re.search(r"GFX_0:\s*\n\s*CLK:\s*(\d+)", r)
+        if pw and ck:
+            samples.append((t, int(pw.group(1)), int(ck.group(1))))
+        stop.wait(max(0.0, 0.7 - (time.time() - t)))
+
+
+def power(args):
+    """Each attention kernel on the workload back to back for a few seconds while amd-smi is
+    sampled: socket power and shader clock under that kernel's load."""
+    import threading
+
+    import torch
+
+    import dynamic_block_sparse_bsa_amd as bsa
+    import gen
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    q, k, v, cfg = gen.make_config(args.config)
+    B, H, S, D = q.shape
+    block, r = cfg["block"], cfg["keep_ratio"]
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    n = bsa.bsa_num_blocks(S, block)
+    rows = B * H * n
+    rp, ci = bsa.bsa_select(qd, kd, block, r)
+    q8, qs = bsa.bsa_quantize_fp8(qd, block)
+    k8, ks = bsa.bsa_quantize_fp8(kd, block)
+    rpf, cif, qf8, qfs, kf8, kfs = bsa.bsa_select_quantize(qd, kd, block, r)
+    vt8, vts = bsa.bsa_quantize_v_fp8(vd, block)
+    rp1 = torch.arange(rows + 1, dtype=torch.int32, device=dev) * n
+    ci1 = torch.arange(n, dtype=torch.int32, device=dev).repeat(rows)
+    out = torch.empty_like(qd)
+    flop = 4.0 * D * kept_flops(rp.cpu().numpy(), ci.cpu().numpy(), S, block)
+    flop1 = 4.0 * D * kept_flops(rp1.cpu().numpy(), ci1.cpu().numpy(), S, block)
+    runs = [
+        ("bf16", flop, lambda: bsa.bsa_forward(qd, kd, vd, block, rp, ci, out=out)),
+        ("fp8_qk", flop, lambda: bsa.bsa_forward_fp8(q8, qs, k8, ks, vd, block, rp, ci, out=out)),
+        ("fp8_full", flop, lambda: bsa.bsa_forward_fp8_full(qf8, qfs, kf8, kfs, vt8, vts, block, rpf, cif, out=out)),
+        ("bf16_dense", flop1, lambda: bsa.bsa_forward(qd, kd, vd, block, rp1, ci1, out=out)),
+    ]
+    torch.cuda.synchronize()
+    samples, stop = [], threading.Event()
+    th = threading.Thread(target=sample_power, args=(stop, samples), daemon=True)
+    th.start()
+    time.sleep(2.0)
+    idle = [(p, c) for _, p, c in samples]
+    for name, fl, f in runs:
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0, calls = time.time(), 0
+        e0.record()
+        while time.time() - t0 < args.power_seconds:
+            for _ in range(5):
+                f()
+            calls += 5
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        ms = e0.elapsed_time(e1) / calls
+        load = [(p, c) for t, p, c in samples if t0 + 1.0 < t < t1]  # skip the ramp
+        line = {
+            "workload": "%s: B=%d H=%d S=%d D=%d block=%d keep=%g" % (args.config, B, H, S, D, block,
+                                                                     1.0 if name == "bf16_dense" else r),
+            "kernel": name, "calls": calls, "attention_ms": round(ms, 4),
+            "kept_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+            "socket_power_w": round(sum(p for p, _ in load) / len(load), 1) if load else None,
+            "gfx_clock_mhz": round(sum(c for _, c in load) / len(load), 1) if load else None,
+            "samples": len(load),
+        }
+        print(json.dumps(line), flush=True)
+        time.sleep(2.0)
+    stop.set()
+    th.join(timeout=15)
+    if idle:
+        print(json.dumps({"idle_socket_power_w": round(sum(p for p, _ in idle) / len(idle), 1),
+                          "idle_gfx_clock_mhz": round(sum(c for _, c in idle) / len(idle), 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +261,10 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="keep_ratio sweep 0.10-0.20 on the 480p, 720p and long shapes instead: one "
                          "JSON line per point with ms, kept TFLOP/s and the error against dense attention")
+    ap.add_argument("--power", action="store_true",
+                    help="instead: run each attention kernel for a few seconds while amd-smi samples "
+                         "socket power and shader clock; one JSON line per kernel")
+    ap.add_argument("--power-seconds", type=float, default=6.0)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the design notes "
@@ -173,6 +272,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args)
+        return
+    if args.power:
+        power(args)
         return
 
     import torch
