@@ -113,6 +113,10 @@ struct Cfg {
     // Direct global->LDS loads move 1 KiB per wave instruction ("segment").
     static constexpr int KRPS = 1024 / KROWB, VRPS = 1024 / VROWB;  // rows per segment
     static constexpr int KSEGW = KTILE / 1024 / NW, VSEGW = VTILE / 1024 / NW;  // per wave
+    // Waves per SIMD that LDS allows (160 KiB per CU, four SIMDs), at most two: one for
+    // 128-dim 64-token blocks (64 KiB per two-wave workgroup), so those may use 512 registers.
+    static constexpr int LDS_WAVES = (160 * 1024 / (2 * STAGE)) * NW / 4;
+    static constexpr int WAVES_PER_SIMD = LDS_WAVES >= 2 ? 2 : 1;
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -131,7 +135,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 template <int D, int BLK, int MODE>
-__global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(Cfg<D, BLK, MODE>::WAVES_PER_SIMD, 2)))
 attn_kernel(const AttnArgs a) {
     using C = Cfg<D, BLK, MODE>;
     constexpr bool FP8 = C::FP8, PV8 = C::PV8;
@@ -230,32 +234,41 @@ attn_kernel(const AttnArgs a) {
     }
     // Loads the sub-tile of nk keys (1 <= nk <= KT) starting at key0. Rows past the end of
     // the sequence re-read its last row; their scores are masked. (The E4M3 V channel rows
-    // are zero padded to whole blocks and never need clamping.)
+    // are zero padded to whole blocks and never need clamping.) The LDS destination of
+    // segment x is wave-uniform, stage + (x*NW + wave) KiB. With many segments per wave it is
+    // formed per load from one opaque scalar, so that the compiler does not keep every
+    // stage/segment combination live in scalar registers (and spill them).
     auto issue_tile = [&](int key0, int nk, char* stage_base) {
         const uint32_t ko = (uint32_t)key0 * C::KROWB;
         const uint32_t vo = PV8 ? (uint32_t)key0 : (uint32_t)key0 * C::VROWB;
         const int last = nk - 1;
+        uint32_t dst = (uint32_t)(stage_base - lds) + wave * 1024;
+        if constexpr (C::KSEGW + C::VSEGW > 8) asm volatile("" : "+s"(dst));
+        // LDS destination of segment x of the tile at byte offset toff within the stage
+        auto seg = [&](int toff, int x) -> char* {
+            if constexpr (C::KSEGW + C::VSEGW > 8) return lds + dst + toff + x * C::NW * 1024;
+            else return stage_base + toff + (x * C::NW + wave) * 1024;
+        };
         if (nk == KT) {
 #pragma unroll
-            for (int x = 0; x < C::KSEGW; ++x) dma16(krsrc, k_src[x], ko, stage_base + (x * C::NW + wave) * 1024);
+            for (int x = 0; x < C::KSEGW; ++x) dma16(krsrc, k_src[x], ko, seg(0, x));
         } else {
 #pragma unroll
             for (int x = 0; x < C::KSEGW; ++x) {
                 const int r = (x * C::NW + wave) * C::KRPS + lane / C::KCH;
                 const int rr = r < last ? r : last;
-                dma16(krsrc, k_src[x] - (r - rr) * C::KROWB, ko, stage_base + (x * C::NW + wave) * 1024);
+                dma16(krsrc, k_src[x] - (r - rr) * C::KROWB, ko, seg(0, x));
             }
         }
         if (PV8 || nk == KT) {
 #pragma unroll
-            for (int x = 0; x < C::VSEGW; ++x)
-                dma16(vrsrc, v_src[x], vo, stage_base + C::KTILE + (x * C::NW + wave) * 1024);
+            for (int x = 0; x < C::VSEGW; ++x) dma16(vrsrc, v_src[x], vo, seg(C::KTILE, x));
         } else {
 #pragma unroll
             for (int x = 0; x < C::VSEGW; ++x) {
                 const int r = (x * C::NW + wave) * C::VRPS + lane / C::VCH;
                 const int rr = r < last ? r : last;
-                dma16(vrsrc, v_src[x] - (r - rr) * C::VROWB, vo, stage_base + C::KTILE + (x * C::NW + wave) * 1024);
+                dma16(vrsrc, v_src[x] - (r - rr) * C::VROWB, vo, seg(C::KTILE, x));
             }
         }
     };
