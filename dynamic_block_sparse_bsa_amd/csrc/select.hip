@@ -20,6 +20,8 @@ namespace bsa {
 namespace {
 
 constexpr int kThreads = 256;
+// Rows of up to 64 * kSelectRegChunks blocks keep their selection keys in registers.
+constexpr int kSelectRegChunks = 16;
 
 // ---- pooling -------------------------------------------------------------------------
 // Thread t handles 16-byte chunk (t % CH) of the row, for tokens t / CH, t / CH + TL, ...
@@ -62,13 +64,15 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(const uint16_t* __restri
 }
 
 // ---- scores + top-k ------------------------------------------------------------------
-// One workgroup per (b*h, group of R query blocks); wave w selects for query block w of
-// the group. Scores live in LDS (R * n floats).
-template <int D>
+// One workgroup per (b*h, group of R query blocks): the pooled keys of the head are read
+// once per group (R rows share each load), and wave w selects for query blocks w, w + 4, ...
+// of the group. Scores live in LDS (R * n floats); during the select a row of up to
+// 64 * kSelectRegChunks blocks keeps its keys in registers (chunk c of lane l: block 64c + l),
+// so the 32 threshold passes need no LDS reads. Longer rows select from LDS.
+template <int D, int R>
 __global__ void __launch_bounds__(kThreads) select_kernel(const float* __restrict__ qbar, const float* __restrict__ kbarT,
                                                           int BH, int n, int kept, float scale,
                                                           int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
-    constexpr int R = kSelectRowsPerGroup;
     extern __shared__ float smem[];
     float* qs = smem;            // [R][D]
     float* sc = smem + R * D;    // [R][n]
@@ -97,50 +101,91 @@ __global__ void __launch_bounds__(kThreads) select_kernel(const float* __restric
     }
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int i = i0 + w;
-    if (w >= R || i >= n) return;
-    uint32_t* key = (uint32_t*)(sc + w * n);
-    for (int j = lane; j < n; j += 64) key[j] = ordered_key(sc[w * n + j]);
-    // (each lane rewrites only the entries it reads below; a wave sees its own writes)
-
-    // Largest T with #(key >= T) >= kept: the kept-th largest key.
-    uint32_t T = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = T | (1u << b);
-        int cnt = 0;
-        for (int j0 = 0; j0 < n; j0 += 64) {
-            const int j = j0 + lane;
-            const bool ge = (j < n) && key[j] >= cand;
-            cnt += __popcll(__ballot(ge));
-        }
-        if (cnt >= kept) T = cand;
-    }
-    int gt = 0;
-    for (int j0 = 0; j0 < n; j0 += 64) {
-        const int j = j0 + lane;
-        gt += __popcll(__ballot((j < n) && key[j] > T));
-    }
-    const int need = kept - gt;  // how many blocks with key == T to take, lowest index first
-    const int64_t row = (int64_t)bh * n + i;
-    int32_t* out = col_idx + row * kept;
+    const int lane = threadIdx.x & 63;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int pos = 0, ties = 0;
-    for (int j0 = 0; j0 < n; j0 += 64) {
-        const int j = j0 + lane;
-        const uint32_t kj = (j < n) ? key[j] : 0u;
-        const bool eq = (j < n) && kj == T;
-        const uint64_t eqm = __ballot(eq);
-        const int tie_rank = ties + __popcll(eqm & below);
-        const bool sel = (j < n) && (kj > T || (eq && tie_rank < need));
-        const uint64_t selm = __ballot(sel);
-        if (sel) out[pos + __popcll(selm & below)] = j;
-        pos += __popcll(selm);
-        ties += __popcll(eqm);
-    }
-    if (lane == 0) {
-        row_ptr[row] = (int32_t)(row * kept);
-        if (row == (int64_t)BH * n - 1) row_ptr[row + 1] = (int32_t)((row + 1) * kept);
+    for (int w = threadIdx.x >> 6; w < R && i0 + w < n; w += kThreads / 64) {
+        const int i = i0 + w;
+        const int64_t row = (int64_t)bh * n + i;
+        int32_t* out = col_idx + row * kept;
+        const float* srow = sc + w * n;
+        if (n <= 64 * kSelectRegChunks) {
+            // Keys of the row in registers, chunk c holding blocks 64c + lane.
+            const int nch = (n + 63) / 64;
+            uint32_t kr[kSelectRegChunks];
+#pragma unroll
+            for (int c = 0; c < kSelectRegChunks; ++c) {
+                const int j = 64 * c + lane;
+                kr[c] = (c < nch && j < n) ? ordered_key(srow[j]) : 0u;
+            }
+            // Largest T with #(key >= T) >= kept: the kept-th largest key. Real keys are >= 1
+            // (ordered_key maps no finite score to 0), so the padding never counts.
+            uint32_t T = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = T | (1u << bit);
+                int cnt = 0;
+#pragma unroll
+                for (int c = 0; c < kSelectRegChunks; ++c)
+                    if (c < nch) cnt += __popcll(__ballot(kr[c] >= cand));
+                if (cnt >= kept) T = cand;
+            }
+            int gt = 0;
+#pragma unroll
+            for (int c = 0; c < kSelectRegChunks; ++c)
+                if (c < nch) gt += __popcll(__ballot(kr[c] > T));
+            const int need = kept - gt;  // how many blocks with key == T to take, lowest index first
+            int pos = 0, ties = 0;
+#pragma unroll
+            for (int c = 0; c < kSelectRegChunks; ++c) {
+                if (c >= nch) break;
+                const int j = 64 * c + lane;
+                const bool valid = j < n;
+                const bool eq = valid && kr[c] == T;
+                const uint64_t eqm = __ballot(eq);
+                const int tie_rank = ties + __popcll(eqm & below);
+                const bool sel = valid && (kr[c] > T || (eq && tie_rank < need));
+                const uint64_t selm = __ballot(sel);
+                if (sel) out[pos + __popcll(selm & below)] = j;
+                pos += __popcll(selm);
+                ties += __popcll(eqm);
+            }
+        } else {
+            uint32_t* key = (uint32_t*)(sc + w * n);
+            for (int j = lane; j < n; j += 64) key[j] = ordered_key(srow[j]);
+            // (each lane rewrites only the entries it reads below; a wave sees its own writes)
+            uint32_t T = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = T | (1u << bit);
+                int cnt = 0;
+                for (int j0 = 0; j0 < n; j0 += 64) {
+                    const int j = j0 + lane;
+                    cnt += __popcll(__ballot((j < n) && key[j] >= cand));
+                }
+                if (cnt >= kept) T = cand;
+            }
+            int gt = 0;
+            for (int j0 = 0; j0 < n; j0 += 64) {
+                const int j = j0 + lane;
+                gt += __popcll(__ballot((j < n) && key[j] > T));
+            }
+            const int need = kept - gt;
+            int pos = 0, ties = 0;
+            for (int j0 = 0; j0 < n; j0 += 64) {
+                const int j = j0 + lane;
+                const uint32_t kj = (j < n) ? key[j] : 0u;
+                const bool eq = (j < n) && kj == T;
+                const uint64_t eqm = __ballot(eq);
+                const int tie_rank = ties + __popcll(eqm & below);
+                const bool sel = (j < n) && (kj > T || (eq && tie_rank < need));
+                const uint64_t selm = __ballot(sel);
+                if (sel) out[pos + __popcll(selm & below)] = j;
+                pos += __popcll(selm);
+                ties += __popcll(eqm);
+            }
+        }
+        if (lane == 0) {
+            row_ptr[row] = (int32_t)(row * kept);
+            if (row == (int64_t)BH * n - 1) row_ptr[row + 1] = (int32_t)((row + 1) * kept);
+        }
     }
 }
 
@@ -216,24 +261,29 @@ hipError_t launch_pool_qk(const void* q, const void* k, int BH, int S, int D, in
     return hipGetLastError();
 }
 
-hipError_t launch_select(const float* qbar, const float* kbarT, int BH, int n, int D, int kept, int32_t* row_ptr,
-                         int32_t* col_idx, hipStream_t stream) {
-    constexpr int R = kSelectRowsPerGroup;
+template <int D, int R>
+static hipError_t launch_select_r(const float* qbar, const float* kbarT, int BH, int n, int kept, int32_t* row_ptr,
+                                  int32_t* col_idx, hipStream_t stream) {
     const int groups = (n + R - 1) / R;
     const size_t smem = sizeof(float) * (size_t)R * (D + n);
     const float scale = 1.0f / sqrtf((float)D);
-    const void* fn = D == 128 ? (const void*)select_kernel<128> : (const void*)select_kernel<64>;
     if (smem > 65536) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipError_t e = hipFuncSetAttribute((const void*)select_kernel<D, R>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)smem);
         if (e != hipSuccess) return e;
     }
-    if (D == 128)
-        hipLaunchKernelGGL(select_kernel<128>, dim3(BH * groups), dim3(kThreads), smem, stream, qbar, kbarT, BH, n, kept,
-                           scale, row_ptr, col_idx);
-    else
-        hipLaunchKernelGGL(select_kernel<64>, dim3(BH * groups), dim3(kThreads), smem, stream, qbar, kbarT, BH, n, kept,
-                           scale, row_ptr, col_idx);
+    hipLaunchKernelGGL((select_kernel<D, R>), dim3(BH * groups), dim3(kThreads), smem, stream, qbar, kbarT, BH, n, kept,
+                       scale, row_ptr, col_idx);
     return hipGetLastError();
+}
+
+hipError_t launch_select(const float* qbar, const float* kbarT, int BH, int n, int D, int kept, int32_t* row_ptr,
+                         int32_t* col_idx, hipStream_t stream) {
+    // Four query blocks per workgroup: measured faster than 8 or 16 (more workgroups in flight
+    // outweigh the extra reads of the pooled keys, which stay in L2).
+    constexpr int R = kSelectRowsPerGroup;
+    if (D == 128) return launch_select_r<128, R>(qbar, kbarT, BH, n, kept, row_ptr, col_idx, stream);
+    return launch_select_r<64, R>(qbar, kbarT, BH, n, kept, row_ptr, col_idx, stream);
 }
 
 hipError_t launch_quantize_fp8(const void* x, int BH, int S, int D, int block, void* codes, float* scale,
