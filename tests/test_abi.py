@@ -163,3 +163,38 @@ def test_full_fp8_calls_check_arguments_on_the_host():
     assert st == 1
     st = lib().bsa_select_quantize(FAKE, FAKE, 1, 1, 1024, 64, 64, 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
     assert st == 3
+
+
+C_CONSUMER = r"""
+#include <stdio.h>
+#include "bsa.h"
+int main(void) {
+    int32_t n = bsa_num_blocks(1000, 128);
+    int32_t k = bsa_num_kept(n, 0.3);
+    bsa_status st = bsa_select(NULL, NULL, 1, 1, 1000, 128, 128, 0.3, NULL, NULL, NULL, 0, NULL);
+    printf("%d %d %d %s\n", (int)n, (int)k, (int)st, bsa_status_string(st));
+    return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/bsa.h compiles as strict C99 and a C program links against libbsa.so."""
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "consumer.c"
+    src.write_text(C_CONSUMER)
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(bsa.lib_path)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+           "-L", libdir, "-lbsa", "-Wl,-rpath," + libdir, "-Wl,-rpath-link,/opt/rocm/lib", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    n, k, st, name = out.stdout.split()
+    assert (int(n), int(k)) == (8, bsa.bsa_num_kept(8, 0.3))
+    assert name == "BSA_ERR_INVALID_ARGUMENT" and int(st) != 0
