@@ -319,3 +319,53 @@ def test_fp8_full_forward_rising_scores_and_ragged_lists():
     expect = oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, rp, ci)
     check_fp8_full(out, expect)
     assert np.all(out[0, 0, block:2 * block] == 0.0)  # row 1 has an empty list
+
+
+def random_case(i):
+    """Shape, keep ratio and input structure drawn from a seeded generator (case i)."""
+    rng = np.random.default_rng(1000 + i)
+    D = int(rng.choice([64, 128]))
+    block = int(rng.choice([64, 128]))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    S = int(rng.integers(1, 2600))
+    r = float(rng.choice([0.05, 0.1, 0.15, 0.2, 0.3, 0.5, 1.0]))
+    alpha = float(rng.choice([0.0, 0.5, 1.0]))
+    grid = None
+    if alpha > 0:  # a (S / w) x w x 1 token grid, w a divisor of S
+        divs = [d for d in range(1, min(S, 64) + 1) if S % d == 0]
+        w = int(rng.choice(divs))
+        grid = (S // w, w, 1)
+    return B, H, S, D, block, r, grid, alpha, 2000 + i
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes_all_paths(i):
+    """Seeded random shapes (ragged tails, both D and block sizes, keep ratios up to dense)
+    through every path: lists, bf16, fp8-QK and full fp8 attention against the oracle."""
+    B, H, S, D, block, r, grid, alpha, seed = random_case(i)
+    q, k, v, qd, kd, vd = run_small(B, H, S, D, block, r, grid, alpha, seed)
+    rp, ci = bsa.bsa_select(qd, kd, block, r)
+    ref = oracle.select(q, k, block, r)
+    check_lists(rp.cpu().numpy(), ci.cpu().numpy(), ref)
+    grp, gci = rp.cpu().numpy(), ci.cpu().numpy()
+
+    out = to_f64(bsa.bsa_forward(qd, kd, vd, block, rp, ci))
+    mx, mean = errors(out, oracle.attention(q, k, v, block, grp, gci))
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, ("bf16", mx, mean)
+
+    q8, qs = bsa.bsa_quantize_fp8(qd, block)
+    k8, ks = bsa.bsa_quantize_fp8(kd, block)
+    oq8, oqs = oracle.quantize_fp8(q, block)
+    ok8, oks = oracle.quantize_fp8(k, block)
+    assert np.array_equal(q8.cpu().numpy(), oq8) and np.array_equal(k8.cpu().numpy(), ok8)
+    out8 = to_f64(bsa.bsa_forward_fp8(q8, qs, k8, ks, vd, block, rp, ci))
+    mx, mean = errors(out8, oracle.attention_fp8(oq8, oqs, ok8, oks, v, block, grp, gci))
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, ("fp8-QK", mx, mean)
+
+    rpf, cif, qf8, qfs, kf8, kfs = bsa.bsa_select_quantize(qd, kd, block, r)
+    assert torch.equal(rpf, rp) and torch.equal(cif, ci)
+    vt8, vts = bsa.bsa_quantize_v_fp8(vd, block)
+    ov8, ovs = oracle.quantize_v_fp8(v)
+    assert np.array_equal(vts.cpu().numpy(), ovs)
+    outf = to_f64(bsa.bsa_forward_fp8_full(qf8, qfs, kf8, kfs, vt8, vts, block, rp, ci))
+    check_fp8_full(outf, oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, grp, gci))
