@@ -369,3 +369,14 @@ def test_random_shapes_all_paths(i):
     assert np.array_equal(vts.cpu().numpy(), ovs)
     outf = to_f64(bsa.bsa_forward_fp8_full(qf8, qfs, kf8, kfs, vt8, vts, block, rp, ci))
     check_fp8_full(outf, oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, grp, gci))
+
+
+@pytest.mark.parametrize("S,block,r", [(1100 * 64 - 13, 64, 0.1), (1030 * 64, 64, 0.02), (1025 * 128 - 1, 128, 0.05)])
+def test_select_long_rows(S, block, r):
+    """Rows of more than 1024 key blocks (the select keeps their keys in LDS, not registers)."""
+    B, H, D = 1, 1, 64
+    q, k, v = gen.make_qkv(B, H, S, D, 77, grid=(S, 1, 1), alpha=1.0)
+    rp, ci = bsa.bsa_select(to_dev(q), to_dev(k), block, r)
+    ref = oracle.select(q, k, block, r)
+    assert oracle.num_blocks(S, block) > 1024
+    check_lists(rp.cpu().numpy(), ci.cpu().numpy(), ref)
