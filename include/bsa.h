@@ -37,6 +37,10 @@
  *     synchronises; it keeps only a per-device table of properties.
  *   - Streams: every compute call is enqueued on hip_stream (a hipStream_t; NULL is the
  *     null stream) and returns before the GPU finishes. Outputs must not alias inputs.
+ *     A call only launches kernels (no memset, no copy, no synchronisation), so a sequence
+ *     of calls can be captured into a HIP graph and replayed; selection with more than
+ *     3968 blocks per sequence (D = 128; 4032 for D = 64) also raises the scoring kernel's
+ *     dynamic LDS limit on its first use, so make one such call before capturing.
  *   - Errors: arguments are checked on the host before any HIP call, so a bad argument
  *     returns an error without touching the GPU and without side effects. Faults on the
  *     device surface at the caller's next synchronisation. No C++ exception crosses this
