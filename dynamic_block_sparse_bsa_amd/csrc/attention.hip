@@ -1,4 +1,4 @@
-// Sparse attention over kept key blocks, bf16 and fp8-QK variants, for gfx950.
+// Sparse attention over kept key blocks for gfx950: bf16, fp8-QK and full fp8 variants.
 //
 // Method: the knowledge card "600倍加速，720p视频实时生成！单卡也能带的动14B模型", section
 // 方法/产品要点, item 动态稀疏量化注意力 (only the activated key blocks are computed; an
@@ -8,10 +8,10 @@
 // Work decomposition
 //   One workgroup per (batch*head, query block); BLK/32 waves, each owning 32 query rows.
 //   The workgroup walks its row of the kept-block list in ascending order, 64 keys
-//   (a "sub-tile") at a time. K and V sub-tiles are staged in LDS, double-buffered: the
-//   next sub-tile's global loads are issued into registers before the current one is
-//   computed and written to the other LDS stage afterwards, so one barrier per sub-tile
-//   suffices.
+//   (a "sub-tile") at a time. K and V sub-tiles are loaded straight from global memory into
+//   LDS (buffer loads with the LDS destination), double-buffered: the next sub-tile's loads
+//   are issued before the current one is computed from the other stage, and one wait plus
+//   one barrier per sub-tile hands the stages over.
 //
 // Per wave and sub-tile
 //   S^T (64 keys x 32 queries) = K . Q^T on 32x32x16 bf16 MFMA (A = K rows from LDS,
@@ -20,9 +20,10 @@
 //   statistics are lane-local except for one exchange with lane^32.
 //   O^T (D x 32 queries) += V^T . P^T on 32x32x16 bf16 MFMA: P^T comes straight from the
 //   S^T accumulators (converted to bf16), V^T from row-major V tiles in LDS through the
-//   transposing ds_read_b64_tr_b16.
-//   The online softmax works in the log2 domain with a lazily raised reference point
-//   (see kSumLimit).
+//   transposing ds_read_b64_tr_b16. The full fp8 mode stores P^T as E4M3 and reads V^T
+//   codes from a transposed, key-permuted V (32x32x64 fp8 MFMA).
+//   The bf16 and fp8-QK modes run the online softmax in the log2 domain with a lazily raised
+//   reference point (see kSumLimit); the full fp8 mode keeps the exact running maximum.
 //
 // LDS layout: K and V tiles are row-major [64 keys][D], 16-byte chunks XOR-swizzled per row
 // so that both the K-operand reads (16 rows, one chunk) and the transposing V reads
