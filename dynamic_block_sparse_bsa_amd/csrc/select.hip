@@ -201,33 +201,43 @@ __global__ void __launch_bounds__(kThreads) quant_kernel(const uint16_t* __restr
     const int cnt = (S - t0) < block ? (S - t0) : block;
     const int64_t base = ((int64_t)bh * S + t0) * D;
     const int chunks = cnt * CH;
+    // One read of the block: a thread's chunks (at most 128 rows * CH / kThreads of them) stay
+    // in registers from the absmax pass to the code pass.
+    constexpr int MAXQ = 128 * CH / kThreads;
+    u32x4 w[MAXQ];
     float amax = 0.0f;
-    for (int q = threadIdx.x; q < chunks; q += kThreads) {
-        u32x4 w = *(const u32x4*)(x + base + 8 * (int64_t)q);
+#pragma unroll
+    for (int it = 0; it < MAXQ; ++it) {
+        const int q = threadIdx.x + it * kThreads;
+        w[it] = q < chunks ? *(const u32x4*)(x + base + 8 * (int64_t)q) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int it = 0; it < MAXQ; ++it)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            amax = fmaxf(amax, fabsf(__uint_as_float(w[e] << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(w[e] & 0xFFFF0000u)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[it][e] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[it][e] & 0xFFFF0000u)));
         }
-    }
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
     __syncthreads();
     amax = wmax[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+    for (int wv = 1; wv < kThreads / 64; ++wv) amax = fmaxf(amax, wmax[wv]);
     const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
     if (threadIdx.x == 0) scale[rowi] = sc;
-    for (int q = threadIdx.x; q < chunks; q += kThreads) {
-        u32x4 w = *(const u32x4*)(x + base + 8 * (int64_t)q);
+#pragma unroll
+    for (int it = 0; it < MAXQ; ++it) {
+        const int q = threadIdx.x + it * kThreads;
+        if (q >= chunks) break;
         u32x2 packed;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             int v = 0;
-            v = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w[2 * e] << 16) / sc,
-                                                __uint_as_float(w[2 * e] & 0xFFFF0000u) / sc, v, false);
-            v = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w[2 * e + 1] << 16) / sc,
-                                                __uint_as_float(w[2 * e + 1] & 0xFFFF0000u) / sc, v, true);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w[it][2 * e] << 16) / sc,
+                                                __uint_as_float(w[it][2 * e] & 0xFFFF0000u) / sc, v, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(w[it][2 * e + 1] << 16) / sc,
+                                                __uint_as_float(w[it][2 * e + 1] & 0xFFFF0000u) / sc, v, true);
             packed[e] = (uint32_t)v;
         }
         *(u32x2*)(codes + base + 8 * (int64_t)q) = packed;
