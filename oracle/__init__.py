@@ -59,6 +59,10 @@ def _load():
     lib.oracle_quantize_v_fp8.argtypes = [P, i32, i32, i32, i32, P, P]
     lib.oracle_attention_fp8_full.restype = None
     lib.oracle_attention_fp8_full.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, i64, P]
+    lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_bf16.argtypes = [f64]
+    lib.oracle_norm_rope.restype = None
+    lib.oracle_norm_rope.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, f64, f64, P, P]
     _lib = lib
     return lib
 
@@ -253,3 +257,28 @@ def attention_fp8_full(q8, q_scale, k8, k_scale, v8, v_scale, block: int, row_pt
     _load().oracle_attention_fp8_full(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale),
                                       B, H, S, D, block, _ptr(row_ptr), _ptr(col_idx), _ptr(t), nt, _ptr(out))
     return out.reshape(B, H, S, D) if t is None else out
+
+
+def round_bf16(x: float) -> int:
+    """Bit pattern of the bf16 nearest to x (ties to even)."""
+    return _load().oracle_round_bf16(float(x))
+
+
+def norm_rope(x, w, grid, eps: float = 1e-6, theta: float = 10000.0):
+    """RMSNorm over each token's H*D channels, then 3D RoPE in each head (bsa_oracle.c).
+
+    x: uint16 [B, S, H, D] bf16 bits, token-major (a projection's output viewed per head);
+    w: uint16 [H*D] bf16 bits; grid: (Gt, Gh, Gw) with Gt*Gh*Gw = S.
+    Returns (y fp64 [B, H, S, D], y16 uint16 [B, H, S, D]: y rounded to bf16)."""
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w).reshape(-1)
+    if x.dtype != np.uint16 or x.ndim != 4 or w.dtype != np.uint16:
+        raise ValueError("expected x uint16 [B, S, H, D] and w uint16 [H*D]")
+    B, S, H, D = x.shape
+    gt, gh, gw = (int(g) for g in grid)
+    if gt * gh * gw != S or w.size != H * D:
+        raise ValueError("grid product must equal S and w must hold H*D values")
+    y = np.empty((B, H, S, D), dtype=np.float64)
+    y16 = np.empty((B, H, S, D), dtype=np.uint16)
+    _load().oracle_norm_rope(_ptr(x), _ptr(w), B, S, H, D, gt, gh, gw, float(eps), float(theta), _ptr(y), _ptr(y16))
+    return y, y16

@@ -383,3 +383,69 @@ void oracle_attention_fp8_full(const uint8_t* q8, const float* q_scale, const ui
         free(qrow); free(x);
     }
 }
+
+/* ---- RMSNorm and 3D RoPE of a Q or K projection ---------------------------------------
+ * [KC] 方法/产品要点, item 高效推理算子, and [AO] 四步拆解, step 4 (融合内核): 3D RoPE and
+ * RMSNorm run as fused kernels, to save temporaries and memory round trips. Neither page
+ * gives a formula, so the following readings define the operation:
+ *   - x is a projection's output, bf16 [B, S, H*D] (token-major); w is bf16 [H*D];
+ *   - RMSNorm over the H*D channels of a token: x_c / sqrt(mean over c of x_c^2 + eps) * w_c;
+ *   - 3D RoPE inside each head: its D channels split into three contiguous segments for the
+ *     frame, height and width axes, of sizes D - 4*floor(D/6), 2*floor(D/6), 2*floor(D/6);
+ *     in a segment of size Da, channels 2i and 2i+1 are turned by the angle
+ *     p * theta^(-2i/Da) (p = the token's coordinate on that axis):
+ *     (u, v) -> (u cos a - v sin a, u sin a + v cos a);
+ *   - token s of the latent grid (Gt, Gh, Gw), row-major, is at (s / (Gh*Gw), (s / Gw) % Gh,
+ *     s % Gw);
+ *   - the result, [B, H, S, D], is rounded once to bf16 (nearest, ties to even).
+ * The block means of the rounded result are oracle_pool of it. */
+
+/* Nearest bf16 to a finite x (ties to even), as its 16-bit pattern. bf16 keeps 8
+ * significant bits down to 2^-126 and a fixed spacing of 2^-133 below. */
+uint16_t oracle_round_bf16(double x) {
+    if (x == 0.0) return signbit(x) ? 0x8000 : 0x0000;
+    int e;
+    (void)frexp(x, &e);               /* 2^(e-1) <= |x| < 2^e */
+    int lsb = e - 8;
+    if (lsb < -133) lsb = -133;
+    double r = ldexp(nearbyint(ldexp(x, -lsb)), lsb);  /* default mode: ties to even */
+    float f = (float)r;                /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+void oracle_norm_rope(const uint16_t* x /* [B, S, H*D] */, const uint16_t* w /* [H*D] */, int32_t B,
+                      int32_t S, int32_t H, int32_t D, int32_t gt, int32_t gh, int32_t gw, double eps,
+                      double theta, double* y /* [B, H, S, D] or NULL */,
+                      uint16_t* y16 /* [B, H, S, D] or NULL */) {
+    const int64_t C = (int64_t)H * D;
+    const int64_t seg[3] = {D - 4 * (D / 6), 2 * (D / 6), 2 * (D / 6)};
+    (void)gt;
+#pragma omp parallel for schedule(static)
+    for (int64_t bs = 0; bs < (int64_t)B * S; ++bs) {
+        const int64_t b = bs / S, s = bs % S;
+        const uint16_t* xr = x + bs * C;
+        double ms = 0.0;
+        for (int64_t c = 0; c < C; ++c) ms += bf16_value(xr[c]) * bf16_value(xr[c]);
+        ms /= (double)C;
+        const double inv = 1.0 / sqrt(ms + eps);
+        const int64_t pos[3] = {s / ((int64_t)gh * gw), (s / gw) % gh, s % gw};
+        for (int64_t h = 0; h < H; ++h) {
+            int64_t off = 0;
+            for (int a = 0; a < 3; ++a) {
+                for (int64_t i = 0; i < seg[a] / 2; ++i) {
+                    const int64_t c0 = h * D + off + 2 * i;
+                    const double u = bf16_value(xr[c0]) * inv * bf16_value(w[c0]);
+                    const double v = bf16_value(xr[c0 + 1]) * inv * bf16_value(w[c0 + 1]);
+                    const double ang = (double)pos[a] * pow(theta, -2.0 * (double)i / (double)seg[a]);
+                    const double r0 = u * cos(ang) - v * sin(ang), r1 = u * sin(ang) + v * cos(ang);
+                    const int64_t o = ((b * H + h) * S + s) * D + off + 2 * i;
+                    if (y) { y[o] = r0; y[o + 1] = r1; }
+                    if (y16) { y16[o] = oracle_round_bf16(r0); y16[o + 1] = oracle_round_bf16(r1); }
+                }
+                off += seg[a];
+            }
+        }
+    }
+}
