@@ -17,7 +17,8 @@ __all__ = [
     "BsaError", "lib_path", "bsa_num_blocks", "bsa_num_kept", "bsa_select_workspace_bytes",
     "bsa_pool", "bsa_select", "bsa_forward", "bsa_quantize_fp8", "bsa_forward_fp8",
     "bsa_check_csr", "bsa_status_string", "bsa_last_error", "bsa_vt_fp8_bytes", "bsa_select_quantize",
-    "bsa_quantize_v_fp8", "bsa_forward_fp8_full",
+    "bsa_quantize_v_fp8", "bsa_forward_fp8_full", "bsa_norm_rope_workspace_bytes", "bsa_norm_rope",
+    "bsa_norm_rope_select_workspace_bytes", "bsa_norm_rope_select",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +62,11 @@ def _load():
         "bsa_select_quantize": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, f64, P, P, P, P, P, P, P, sz, P]),
         "bsa_quantize_v_fp8": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P]),
         "bsa_forward_fp8_full": (ctypes.c_int, [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]),
+        "bsa_norm_rope_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "bsa_norm_rope": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, i32, i32, i32, f64, f64, P, P, P, sz, P]),
+        "bsa_norm_rope_select_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "bsa_norm_rope_select": (ctypes.c_int, [P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f64, f64, f64,
+                                                P, P, P, P, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -296,3 +302,74 @@ def bsa_status_string(status: int) -> str:
 
 def bsa_last_error() -> str:
     return _load().bsa_last_error().decode()
+
+
+def bsa_norm_rope_workspace_bytes(B, H, S, D) -> int:
+    return _load().bsa_norm_rope_workspace_bytes(B, H, S, D)
+
+
+def bsa_norm_rope_select_workspace_bytes(B, H, S, D, block) -> int:
+    return _load().bsa_norm_rope_select_workspace_bytes(B, H, S, D, block)
+
+
+def _projection(x, w, name):
+    _dev_tensor(x, name, (torch.bfloat16,))
+    _dev_tensor(w, "w" + name[1:], (torch.bfloat16,), ndim=1)
+    B, S, H, D = x.shape
+    if w.numel() != H * D:
+        raise ValueError("%s must hold H*D = %d weights" % ("w" + name[1:], H * D))
+    return B, S, H, D
+
+
+def bsa_norm_rope(x, weight, block: int, grid, eps: float = 1e-6, theta: float = 10000.0, means: bool = True,
+                  out=None, xbar=None, workspace=None):
+    """RMSNorm over each token's H*D channels, 3D RoPE per head, written head-major.
+
+    x: bf16 [B, S, H, D] (a projection's output viewed per head, token-major); weight: bf16
+    [H*D]; grid: (Gt, Gh, Gw) with Gt*Gh*Gw = S. Returns out bf16 [B, H, S, D] and, if
+    means, the fp32 block means [B, H, n, D] of out (else None)."""
+    B, S, H, D = _projection(x, weight, "x")
+    gt, gh, gw = (int(g) for g in grid)
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=x.device)
+    ws_bytes = 0
+    if means:
+        n = bsa_num_blocks(S, block)
+        if xbar is None:
+            xbar = torch.empty((B, H, n, D), dtype=torch.float32, device=x.device)
+        ws_bytes = bsa_norm_rope_workspace_bytes(B, H, S, D)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    else:
+        xbar = None
+    _check(_load().bsa_norm_rope(_p(x), _p(weight), B, H, S, D, block, gt, gh, gw, float(eps), float(theta), _p(out),
+                                 _p(xbar) if xbar is not None else None,
+                                 _p(workspace) if workspace is not None else None,
+                                 workspace.numel() if workspace is not None else 0, _stream(x)))
+    return out, xbar
+
+
+def bsa_norm_rope_select(xq, xk, wq, wk, block: int, grid, keep_ratio: float, eps: float = 1e-6,
+                         theta: float = 10000.0, workspace=None):
+    """bsa_norm_rope of both projections and bsa_select's lists from the fused means:
+    returns (q bf16 [B, H, S, D], k bf16 [B, H, S, D], row_ptr, col_idx)."""
+    B, S, H, D = _projection(xq, wq, "xq")
+    if _projection(xk, wk, "xk") != (B, S, H, D):
+        raise ValueError("xq and xk shapes differ")
+    gt, gh, gw = (int(g) for g in grid)
+    n = bsa_num_blocks(S, block)
+    kept = bsa_num_kept(n, keep_ratio)
+    if kept == 0:
+        raise BsaError(1, "keep_ratio must be in (0, 1] (got %r)" % (keep_ratio,))
+    q = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=xq.device)
+    k = torch.empty_like(q)
+    rows = B * H * n
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=xq.device)
+    col_idx = torch.empty(rows * kept, dtype=torch.int32, device=xq.device)
+    ws_bytes = bsa_norm_rope_select_workspace_bytes(B, H, S, D, block)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=xq.device)
+    _check(_load().bsa_norm_rope_select(_p(xq), _p(xk), _p(wq), _p(wk), B, H, S, D, block, gt, gh, gw, float(eps),
+                                        float(theta), float(keep_ratio), _p(q), _p(k), _p(row_ptr), _p(col_idx),
+                                        _p(workspace), workspace.numel(), _stream(xq)))
+    return q, k, row_ptr, col_idx

@@ -6,7 +6,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsa.so")
-SOURCES = ["attention.hip", "select.hip", "fp8.hip", "bsa_api.hip"]
+SOURCES = ["attention.hip", "select.hip", "fp8.hip", "normrope.hip", "bsa_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-strict-aliasing",

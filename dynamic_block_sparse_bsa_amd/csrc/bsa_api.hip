@@ -87,6 +87,48 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr double kLog2e = 1.4426950408889634;
 
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + bn && y < x + an;
+}
+
+// Checks shared by the fused RMSNorm + RoPE calls (one projection).
+bsa_status check_norm_rope(const void* x, const void* w, const void* out, int32_t B, int32_t H, int32_t S, int32_t D,
+                           int32_t block, int32_t gt, int32_t gh, int32_t gw, double eps, double theta) {
+    bsa_status st = check_shape(B, H, S, D, block);
+    if (st != BSA_OK) return st;
+    if ((int64_t)H * D > bsa::kNormRopeMaxChannels)
+        return fail(BSA_ERR_UNSUPPORTED, "H*D must be at most %d (got %lld)", bsa::kNormRopeMaxChannels, (long long)H * D);
+    if (!x || !w || !out) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "x, weight and out must be 16-byte aligned");
+    if (gt < 1 || gh < 1 || gw < 1 || (int64_t)gt * gh * gw != S)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "grid %d x %d x %d does not hold S = %d tokens", gt, gh, gw, S);
+    if (!(eps >= 0.0) || !isfinite(eps)) return fail(BSA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    if (!(theta > 0.0) || !isfinite(theta)) return fail(BSA_ERR_INVALID_ARGUMENT, "theta must be finite and > 0");
+    const size_t tensor = (size_t)B * H * S * D * 2;
+    if (overlaps(out, tensor, x, tensor) || overlaps(out, tensor, w, (size_t)H * D * 2))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "out must not overlap x or weight");
+    return BSA_OK;
+}
+
+bsa::NormRopeArgs norm_rope_args(const void* x, const void* w, void* out, float* partial, int32_t B, int32_t H, int32_t S,
+                                 int32_t gh, int32_t gw, double eps, double theta) {
+    bsa::NormRopeArgs a;
+    a.x = x;
+    a.w = w;
+    a.out = out;
+    a.partial = partial;
+    a.B = B;
+    a.H = H;
+    a.S = S;
+    a.gh = gh;
+    a.gw = gw;
+    a.eps = (float)eps;
+    a.theta = theta;
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,6 +294,78 @@ bsa_status bsa_quantize_fp8(const void* x, int32_t B, int32_t H, int32_t S, int3
     if ((st = check_device()) != BSA_OK) return st;
     return hip_result(bsa::launch_quantize_fp8(x, B * H, S, D, block, x_e4m3, scale, as_stream(hip_stream)),
                       "quantize launch");
+}
+
+size_t bsa_norm_rope_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D) {
+    if (B < 1 || H < 1 || S < 1 || D < 1) return 0;
+    const size_t chunks = ((size_t)S + bsa::kNormRopeTokens - 1) / bsa::kNormRopeTokens;
+    return round_up((size_t)B * chunks * H * D * sizeof(float), 256);
+}
+
+size_t bsa_norm_rope_select_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t block) {
+    const size_t part = bsa_norm_rope_workspace_bytes(B, H, S, D);
+    const size_t means = bsa_select_workspace_bytes(B, H, S, D, block);
+    if (part == 0 || means == 0) return 0;
+    return 2 * part + means;
+}
+
+bsa_status bsa_norm_rope(const void* x, const void* weight, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                         int32_t grid_t, int32_t grid_h, int32_t grid_w, double eps, double theta, void* out,
+                         float* xbar, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    bsa_status st = check_norm_rope(x, weight, out, B, H, S, D, block, grid_t, grid_h, grid_w, eps, theta);
+    if (st != BSA_OK) return st;
+    if (xbar) {
+        if (!workspace) return fail(BSA_ERR_INVALID_ARGUMENT, "null workspace");
+        if (!aligned16(workspace) || ((uintptr_t)xbar & 3u))
+            return fail(BSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte and xbar 4-byte aligned");
+        const size_t need = bsa_norm_rope_workspace_bytes(B, H, S, D);
+        if (workspace_bytes < need) return fail(BSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    }
+    if ((st = check_device()) != BSA_OK) return st;
+    hipStream_t s = as_stream(hip_stream);
+    bsa::NormRopeArgs a = norm_rope_args(x, weight, out, xbar ? (float*)workspace : nullptr, B, H, S, grid_h, grid_w, eps, theta);
+    if ((st = hip_result(bsa::launch_norm_rope(a, D, s), "norm/rope launch")) != BSA_OK) return st;
+    if (!xbar) return BSA_OK;
+    return hip_result(bsa::launch_norm_rope_means((const float*)workspace, B, H, S, D, block, xbar, false, s), "means launch");
+}
+
+bsa_status bsa_norm_rope_select(const void* xq, const void* xk, const void* wq, const void* wk, int32_t B, int32_t H,
+                                int32_t S, int32_t D, int32_t block, int32_t grid_t, int32_t grid_h, int32_t grid_w,
+                                double eps, double theta, double keep_ratio, void* q_out, void* k_out, int32_t* row_ptr,
+                                int32_t* col_idx, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    bsa_status st = check_norm_rope(xq, wq, q_out, B, H, S, D, block, grid_t, grid_h, grid_w, eps, theta);
+    if (st != BSA_OK) return st;
+    if ((st = check_norm_rope(xk, wk, k_out, B, H, S, D, block, grid_t, grid_h, grid_w, eps, theta)) != BSA_OK) return st;
+    if (!row_ptr || !col_idx || !workspace) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u)) return fail(BSA_ERR_INVALID_ARGUMENT, "misaligned CSR arrays");
+    const size_t tensor = (size_t)B * H * S * D * 2;
+    if (overlaps(q_out, tensor, k_out, tensor) || overlaps(q_out, tensor, xk, tensor) || overlaps(k_out, tensor, xq, tensor) ||
+        overlaps(q_out, tensor, wk, (size_t)H * D * 2) || overlaps(k_out, tensor, wq, (size_t)H * D * 2))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "outputs must not overlap the inputs or each other");
+    const int32_t n = bsa_num_blocks(S, block);
+    const int32_t kept = bsa_num_kept(n, keep_ratio);
+    if (kept == 0) return fail(BSA_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1] (got %g)", keep_ratio);
+    if (n > bsa::kMaxSelectBlocks) return fail(BSA_ERR_UNSUPPORTED, "bsa_norm_rope_select supports at most %d blocks per sequence (got %d)", bsa::kMaxSelectBlocks, n);
+    if ((int64_t)B * H * n * kept >= ((int64_t)1 << 31)) return fail(BSA_ERR_UNSUPPORTED, "kept-block list too long for int32 indices");
+    const size_t need = bsa_norm_rope_select_workspace_bytes(B, H, S, D, block);
+    if (workspace_bytes < need) return fail(BSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    if ((st = check_device()) != BSA_OK) return st;
+    const size_t part = bsa_norm_rope_workspace_bytes(B, H, S, D);
+    float* qpart = (float*)workspace;
+    float* kpart = (float*)((char*)workspace + part);
+    float* qbar = (float*)((char*)workspace + 2 * part);
+    float* kbarT = qbar + (size_t)B * H * n * D;
+    hipStream_t s = as_stream(hip_stream);
+    bsa::NormRopeArgs aq = norm_rope_args(xq, wq, q_out, qpart, B, H, S, grid_h, grid_w, eps, theta);
+    bsa::NormRopeArgs ak = norm_rope_args(xk, wk, k_out, kpart, B, H, S, grid_h, grid_w, eps, theta);
+    if ((st = hip_result(bsa::launch_norm_rope(aq, D, s), "norm/rope launch")) != BSA_OK) return st;
+    if ((st = hip_result(bsa::launch_norm_rope(ak, D, s), "norm/rope launch")) != BSA_OK) return st;
+    if ((st = hip_result(bsa::launch_norm_rope_means(qpart, B, H, S, D, block, qbar, false, s), "means launch")) != BSA_OK)
+        return st;
+    if ((st = hip_result(bsa::launch_norm_rope_means(kpart, B, H, S, D, block, kbarT, true, s), "means launch")) != BSA_OK)
+        return st;
+    return hip_result(bsa::launch_select(qbar, kbarT, B * H, n, D, kept, row_ptr, col_idx, s), "select launch");
 }
 
 bsa_status bsa_check_csr(const int32_t* row_ptr, const int32_t* col_idx, int32_t rows, int32_t n_blocks) {

@@ -46,6 +46,23 @@ hipError_t launch_select(const float* qbar, const float* kbarT, int BH, int n, i
 hipError_t launch_quantize_fp8(const void* x, int BH, int S, int D, int block, void* codes, float* scale,
                                hipStream_t stream);
 
+// Fused RMSNorm + 3D RoPE + head-major transpose (+ partial block sums) of a projection.
+struct NormRopeArgs {
+    const void* x;    // bf16 [B, S, H*D], token-major
+    const void* w;    // bf16 [H*D]
+    void* out;        // bf16 [B, H, S, D]
+    float* partial;   // fp32 [B, ceil(S / kNormRopeTokens), H*D] sums of out, or null
+    int B, H, S, gh, gw;  // gh, gw: height and width of the latent grid
+    float eps;
+    double theta;
+};
+constexpr int kNormRopeTokens = 32;    // tokens per workgroup (and per partial sum)
+constexpr int kNormRopeMaxChannels = 8192;  // H*D limit (16 chunks of 8 per lane)
+hipError_t launch_norm_rope(const NormRopeArgs& a, int D, hipStream_t stream);
+// Block means from the partial sums: [B, H, n, D], or [B, H, D, n] if transposed.
+hipError_t launch_norm_rope_means(const float* partial, int B, int H, int S, int D, int block, float* xbar,
+                                  bool transposed, hipStream_t stream);
+
 constexpr int kSelectRowsPerGroup = 4;
 constexpr int kMaxSelectBlocks = 8192;
 

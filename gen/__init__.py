@@ -18,6 +18,10 @@ Recipe (stated as a reading, since the pages give no activation statistics):
       (t, h, w) phases agree -- the spatial locality that makes block selection useful;
   G4  X = N(0,1) noise (independent per tensor) + alpha * phi(s) M, rounded to bf16
       (round to nearest even). The tiny configuration is pure noise.
+  G5  the inputs of the fused RMSNorm + 3D RoPE call are Q and K projections before the
+      head split: X_q and X_k of G4 laid out token-major [B, S, H, D] (a linear layer's
+      output viewed per head), and RMSNorm weights 1 + 0.1 * N(0, 1) per channel, rounded
+      to bf16, from their own seed.
 Streams: numpy SeedSequence(seed) spawns 1 + 3*B*H child seeds; child 0 draws M (when a
 grid is given), child 1 + t*B*H + (b*H + h) draws the [S, D] noise of tensor t (Q, K, V in
 that order) for batch b, head h. The streams are independent of how many threads fill
@@ -104,3 +108,15 @@ def make_config(name: str):
     cfg = dict(CONFIGS[name])
     q, k, v = make_qkv(cfg["B"], cfg["H"], cfg["S"], cfg["D"], cfg["seed"], cfg["grid"], cfg["alpha"])
     return q, k, v, cfg
+
+
+def make_projections(B: int, S: int, H: int, D: int, seed: int, grid=None, alpha: float = 0.0):
+    """(x_q, x_k): G4's Q and K, token-major uint16 bf16 bits [B, S, H, D] (G5)."""
+    q, k, _ = make_qkv(B, H, S, D, seed, grid, alpha)
+    return np.ascontiguousarray(q.transpose(0, 2, 1, 3)), np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+
+
+def make_norm_weight(C: int, seed: int) -> np.ndarray:
+    """RMSNorm weights 1 + 0.1 * N(0, 1), bf16 bits [C] (G5)."""
+    w = 1.0 + 0.1 * np.random.default_rng(seed).standard_normal(C)
+    return f32_to_bf16_bits(w.astype(np.float32))

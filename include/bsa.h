@@ -40,7 +40,8 @@
  *     A call only launches kernels (no memset, no copy, no synchronisation), so a sequence
  *     of calls can be captured into a HIP graph and replayed; selection with more than
  *     3968 blocks per sequence (D = 128; 4032 for D = 64) also raises the scoring kernel's
- *     dynamic LDS limit on its first use, so make one such call before capturing.
+ *     dynamic LDS limit on its first use, so make one such call before capturing; so do
+ *     bsa_norm_rope with means and bsa_norm_rope_select when H*D > 4096.
  *   - Errors: arguments are checked on the host before any HIP call, so a bad argument
  *     returns an error without touching the GPU and without side effects. Faults on the
  *     device surface at the caller's next synchronisation. No C++ exception crosses this
@@ -183,6 +184,63 @@ bsa_status bsa_forward_fp8_full(const void* q_e4m3, const float* q_scale, const 
                                 int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
                                 const int32_t* row_ptr, const int32_t* col_idx, void* out,
                                 void* hip_stream);
+
+/* ---- Fused RMSNorm + 3D RoPE + block means ------------------------------------------------
+ * Source: [KC] section 方法/产品要点, item 高效推理算子, and [AO] section 四步拆解, step 4:
+ * 3D RoPE and RMSNorm run as fused kernels, to save temporaries and memory round trips. The
+ * pages give no formula; this library defines the operation as follows (the oracle's
+ * definition too). For a Q or K projection x (bf16 [B, S, H*D], token-major, as a linear
+ * layer writes it) and RMSNorm weights w (bf16 [H*D]):
+ *   z[b,s,c]   = x[b,s,c] / sqrt(mean over c' of x[b,s,c']^2 + eps) * w[c]   (all H*D channels)
+ *   out[b,h,s] = the D channels z[b,s,h*D .. h*D+D) with each adjacent pair (2i, 2i+1) of
+ *                three contiguous segments -- frame, height, width axes, of D - 4*floor(D/6),
+ *                2*floor(D/6) and 2*floor(D/6) channels -- turned by p * theta^(-2i/Da)
+ *                radians, (u, v) -> (u cos - v sin, u sin + v cos), where p is the token's
+ *                coordinate on that axis and Da the segment size; token s of the latent grid
+ *                (grid_t, grid_h, grid_w) is at (s / (grid_h*grid_w), (s / grid_w) % grid_h,
+ *                s % grid_w);
+ * computed in fp32 (rotation angles reduced in fp64) and rounded once to bf16; out is
+ * head-major [B, H, S, D], the layout bsa_forward takes. The block means are the means of the
+ * written bf16 values (what bsa_pool(out) gives, up to fp32 summation order), fp32 sums in a
+ * fixed order. Supported: the shapes above with H*D <= 8192 and grid_t*grid_h*grid_w == S. */
+
+/* Bytes of device workspace for bsa_norm_rope with means: fp32 partial sums,
+ * B * ceil(S/32) * H*D * 4, rounded up to 256. 0 on invalid shape. Host only. */
+size_t bsa_norm_rope_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D);
+
+/* One projection: out = RMSNorm + 3D RoPE of x, head-major, and (if xbar is not NULL) its
+ * block means.
+ *   x: bf16 [B, S, H*D] (device).   weight: bf16 [H*D] (device).
+ *   eps >= 0 and theta > 0 (finite); the usual values are 1e-6 and 10000.
+ *   out: bf16 [B, H, S, D] (device); must not overlap x or weight.
+ *   xbar: fp32 [B, H, n, D] (device) or NULL; workspace: at least
+ *   bsa_norm_rope_workspace_bytes() when xbar is not NULL (ignored otherwise).
+ * Pointers x, weight, out and workspace 16-byte aligned, xbar 4-byte aligned.
+ * Errors: INVALID_ARGUMENT (null/misaligned pointer, overlap, grid product != S, bad eps
+ * or theta), UNSUPPORTED (shape, H*D > 8192), WORKSPACE_TOO_SMALL, NO_DEVICE, HIP. */
+bsa_status bsa_norm_rope(const void* x, const void* weight, int32_t B, int32_t H, int32_t S,
+                         int32_t D, int32_t block, int32_t grid_t, int32_t grid_h, int32_t grid_w,
+                         double eps, double theta, void* out, float* xbar, void* workspace,
+                         size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of device workspace bsa_norm_rope_select needs: two sets of partial sums and the
+ * fp32 block means of Q and K, rounded up to 256. 0 on invalid shape. Host only. */
+size_t bsa_norm_rope_select_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t block);
+
+/* Both projections and the selection from one read of each: q_out and k_out as
+ * bsa_norm_rope writes them (xq with wq, xk with wk), and the kept-block lists that
+ * bsa_select(q_out, k_out, ...) would give, scored from the fused block means.
+ *   xq, xk: bf16 [B, S, H*D]; wq, wk: bf16 [H*D]; q_out, k_out: bf16 [B, H, S, D];
+ *   row_ptr, col_idx, keep_ratio: as bsa_select; workspace: at least
+ *   bsa_norm_rope_select_workspace_bytes(). All device memory; outputs must not overlap
+ *   inputs or each other.
+ * Errors: as bsa_norm_rope and bsa_select (n <= 8192). */
+bsa_status bsa_norm_rope_select(const void* xq, const void* xk, const void* wq, const void* wk,
+                                int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                                int32_t grid_t, int32_t grid_h, int32_t grid_w, double eps,
+                                double theta, double keep_ratio, void* q_out, void* k_out,
+                                int32_t* row_ptr, int32_t* col_idx, void* workspace,
+                                size_t workspace_bytes, void* hip_stream);
 
 /* Host-side validator for a CSR held in host memory: row_ptr[0] == 0, non-decreasing,
  * every row's indices strictly ascending in [0, n_blocks). Returns BSA_OK or

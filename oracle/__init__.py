@@ -264,12 +264,13 @@ def round_bf16(x: float) -> int:
     return _load().oracle_round_bf16(float(x))
 
 
-def norm_rope(x, w, grid, eps: float = 1e-6, theta: float = 10000.0):
+def norm_rope(x, w, grid, eps: float = 1e-6, theta: float = 10000.0, exact: bool = True):
     """RMSNorm over each token's H*D channels, then 3D RoPE in each head (bsa_oracle.c).
 
     x: uint16 [B, S, H, D] bf16 bits, token-major (a projection's output viewed per head);
     w: uint16 [H*D] bf16 bits; grid: (Gt, Gh, Gw) with Gt*Gh*Gw = S.
-    Returns (y fp64 [B, H, S, D], y16 uint16 [B, H, S, D]: y rounded to bf16)."""
+    Returns (y fp64 [B, H, S, D], y16 uint16 [B, H, S, D]: y rounded to bf16); y is None
+    when exact is False (large inputs)."""
     x = np.ascontiguousarray(x)
     w = np.ascontiguousarray(w).reshape(-1)
     if x.dtype != np.uint16 or x.ndim != 4 or w.dtype != np.uint16:
@@ -278,7 +279,7 @@ def norm_rope(x, w, grid, eps: float = 1e-6, theta: float = 10000.0):
     gt, gh, gw = (int(g) for g in grid)
     if gt * gh * gw != S or w.size != H * D:
         raise ValueError("grid product must equal S and w must hold H*D values")
-    y = np.empty((B, H, S, D), dtype=np.float64)
+    y = np.empty((B, H, S, D), dtype=np.float64) if exact else None
     y16 = np.empty((B, H, S, D), dtype=np.uint16)
     _load().oracle_norm_rope(_ptr(x), _ptr(w), B, S, H, D, gt, gh, gw, float(eps), float(theta), _ptr(y), _ptr(y16))
     return y, y16

@@ -198,3 +198,53 @@ def test_header_is_plain_c_and_links(tmp_path):
     n, k, st, name = out.stdout.split()
     assert (int(n), int(k)) == (8, bsa.bsa_num_kept(8, 0.3))
     assert name == "BSA_ERR_INVALID_ARGUMENT" and int(st) != 0
+
+
+def test_norm_rope_workspace_bytes():
+    # partial sums of 32-token chunks: B * ceil(S/32) * H*D floats, rounded up to 256
+    assert bsa.bsa_norm_rope_workspace_bytes(1, 40, 75600, 128) == 2363 * 5120 * 4
+    assert bsa.bsa_norm_rope_workspace_bytes(2, 1, 33, 64) == 2 * 2 * 64 * 4  # two chunks per sequence
+    assert bsa.bsa_norm_rope_workspace_bytes(1, 1, 1, 64) == 256
+    assert bsa.bsa_norm_rope_workspace_bytes(0, 1, 1, 64) == 0
+    sel = bsa.bsa_select_workspace_bytes(1, 40, 75600, 128, 128)
+    assert bsa.bsa_norm_rope_select_workspace_bytes(1, 40, 75600, 128, 128) == 2 * 2363 * 5120 * 4 + sel
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(B=0), 1), (dict(D=96), 2), (dict(block=32), 2),
+    (dict(H=65), 2),                                    # H*D = 8320 > 8192
+    (dict(x=None), 1), (dict(w=ctypes.c_void_p(0x20008)), 1), (dict(out=None), 1),
+    (dict(gt=2), 1), (dict(gh=0), 1),                   # grid does not hold S tokens
+    (dict(eps=-1e-6), 1), (dict(eps=float("inf")), 1), (dict(theta=0.0), 1), (dict(theta=float("nan")), 1),
+    (dict(out=ctypes.c_void_p(0x10000 + 4096)), 1),     # out overlaps x
+    (dict(ws=None), 1), (dict(ws_bytes=16), 3), (dict(xbar=ctypes.c_void_p(0x60002)), 1),
+])
+def test_norm_rope_rejects_bad_arguments(args, status):
+    a = dict(x=ctypes.c_void_p(0x10000), w=ctypes.c_void_p(0x20000), B=1, H=4, S=12, D=128, block=64, gt=1, gh=3,
+             gw=4, eps=1e-6, theta=1e4, out=ctypes.c_void_p(0x1000000), xbar=ctypes.c_void_p(0x60000), ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(args)
+    st = lib().bsa_norm_rope(a["x"], a["w"], a["B"], a["H"], a["S"], a["D"], a["block"], a["gt"], a["gh"], a["gw"],
+                             a["eps"], a["theta"], a["out"], a["xbar"], a["ws"], a["ws_bytes"], None)
+    assert st == status, bsa.bsa_last_error()
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(r=0.0), 1), (dict(r=1.5), 1), (dict(rp=None), 1), (dict(ws_bytes=1024), 3),
+    (dict(k_out=ctypes.c_void_p(0x1000000 + 64)), 1),    # q_out and k_out overlap
+    (dict(k_out=ctypes.c_void_p(0x10000)), 1),           # k_out overlaps xq
+    (dict(gw=5), 1),
+    # too many blocks for selection (tensors far apart, so only the block count fails)
+    (dict(S=8193 * 64, gt=8193, gh=64, gw=1, xq=ctypes.c_void_p(1 << 32), xk=ctypes.c_void_p(2 << 32),
+          q_out=ctypes.c_void_p(3 << 32), k_out=ctypes.c_void_p(4 << 32)), 2),
+])
+def test_norm_rope_select_rejects_bad_arguments(args, status):
+    a = dict(xq=ctypes.c_void_p(0x10000), xk=ctypes.c_void_p(0x100000), wq=ctypes.c_void_p(0x20000),
+             wk=ctypes.c_void_p(0x30000), B=1, H=4, S=12, D=128, block=64, gt=1, gh=3, gw=4, eps=1e-6, theta=1e4,
+             r=0.5, q_out=ctypes.c_void_p(0x1000000), k_out=ctypes.c_void_p(0x2000000), rp=FAKE, ci=FAKE, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(args)
+    st = lib().bsa_norm_rope_select(a["xq"], a["xk"], a["wq"], a["wk"], a["B"], a["H"], a["S"], a["D"], a["block"],
+                                    a["gt"], a["gh"], a["gw"], a["eps"], a["theta"], a["r"], a["q_out"], a["k_out"],
+                                    a["rp"], a["ci"], a["ws"], a["ws_bytes"], None)
+    assert st == status, bsa.bsa_last_error()
