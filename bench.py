@@ -152,6 +152,70 @@ def sweep(args):
         torch.cuda.empty_cache()
 
 
+def norm_rope(args):
+    """The fused RMSNorm + 3D RoPE + block means call on each shape's Q/K projections (the
+    pages' fused-kernel item): ms per call and HBM GB/s against the 8 TB/s peak for one
+    projection (bsa_norm_rope), and ms for both projections plus the selection
+    (bsa_norm_rope_select). Algorithmic bytes per projection: x read once and out written
+    once (2 * B*S*H*D * 2), plus the weights and the fp32 block means."""
+    import torch
+
+    import dynamic_block_sparse_bsa_amd as bsa
+    import gen
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    reps = max(2, args.steps)
+    for name in ("480p", "720p", "long"):
+        cfg = gen.CONFIGS[name]
+        B, H, S, D, block, grid = cfg["B"], cfg["H"], cfg["S"], cfg["D"], cfg["block"], cfg["grid"]
+        xq, xk = gen.make_projections(B, S, H, D, cfg["seed"], grid, cfg["alpha"])
+        to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        xqd, xkd = to_dev(xq), to_dev(xk)
+        del xq, xk
+        wq, wk = to_dev(gen.make_norm_weight(H * D, 1)), to_dev(gen.make_norm_weight(H * D, 2))
+        n = bsa.bsa_num_blocks(S, block)
+        out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=dev)
+        xbar = torch.empty((B, H, n, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(bsa.bsa_norm_rope_workspace_bytes(B, H, S, D), dtype=torch.uint8, device=dev)
+        ws2 = torch.empty(bsa.bsa_norm_rope_select_workspace_bytes(B, H, S, D, block), dtype=torch.uint8, device=dev)
+        one = lambda: bsa.bsa_norm_rope(xqd, wq, block, grid, out=out, xbar=xbar, workspace=ws)
+        both = lambda: bsa.bsa_norm_rope_select(xqd, xkd, wq, wk, block, grid, cfg["keep_ratio"], workspace=ws2)
+        for _ in range(args.warmup):
+            one()
+            both()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            one()
+        ev[1].record(stream)
+        for _ in range(reps):
+            both()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        one_ms = ev[0].elapsed_time(ev[1]) / reps
+        both_ms = ev[1].elapsed_time(ev[2]) / reps
+        nbytes = 2 * B * S * H * D * 2 + H * D * 2 + B * H * n * D * 4
+        gbs = nbytes / (one_ms * 1e-3) / 1e9
+        line = {
+            "workload": "norm_rope %s: B=%d H=%d S=%d D=%d grid=%dx%dx%d block=%d" % ((name, B, H, S, D) + tuple(grid) + (block,)),
+            "norm_rope_ms": round(one_ms, 4), "bytes": nbytes, "gb_per_s": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "norm_rope_select_ms": round(both_ms, 4), "keep_ratio": cfg["keep_ratio"],
+        }
+        print(json.dumps(line), flush=True)
+        del xqd, xkd, out, xbar, ws, ws2
+        torch.cuda.empty_cache()
+    if args.calib_copy_mib:
+        x = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(x).copy_(x)
+        torch.cuda.synchronize()
+
+
 def sample_power(stop, samples):
     """Append (time, socket watts, GFX clock MHz) from amd-smi about once a second until stop is set."""
     import re
@@ -265,6 +329,9 @@ def main():
                     help="instead: run each attention kernel for a few seconds while amd-smi samples "
                          "socket power and shader clock; one JSON line per kernel")
     ap.add_argument("--power-seconds", type=float, default=6.0)
+    ap.add_argument("--norm-rope", action="store_true",
+                    help="instead: time the fused RMSNorm + 3D RoPE + block-means call (one projection, "
+                         "and both plus the selection) on the 480p, 720p and long shapes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the design notes "
@@ -275,6 +342,9 @@ def main():
         return
     if args.power:
         power(args)
+        return
+    if args.norm_rope:
+        norm_rope(args)
         return
 
     import torch
