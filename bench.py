@@ -152,6 +152,30 @@ def sweep(args):
         torch.cuda.empty_cache()
 
 
+def norm_rope_cpu_baseline(cfg, frames=2):
+    """The oracle's RMSNorm + 3D RoPE and block means of one projection on this host, on the
+    first `frames` latent frames of the shape, scaled to the whole sequence."""
+    import gen
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    B, H, D, block = cfg["B"], cfg["H"], cfg["D"], cfg["block"]
+    grid = (frames,) + tuple(cfg["grid"][1:])
+    S = int(np.prod(grid))
+    xq, _ = gen.make_projections(B, S, H, D, cfg["seed"], grid, cfg["alpha"])
+    w = gen.make_norm_weight(H * D, 1)
+    t0 = time.perf_counter()
+    _, y16 = oracle.norm_rope(xq, w, grid, exact=False)
+    oracle.pool(y16, block)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(dt * cfg["S"] / S * 1e3, 1), "unit": "ms/projection", "cores": int(os.environ["OMP_NUM_THREADS"]),
+        "kind": "oracle",
+        "sample": "%d of %d frames (%d tokens, %.2f s), scaled to the whole sequence" % (frames, cfg["grid"][0], S, dt),
+    }
+
+
 def norm_rope(args):
     """The fused RMSNorm + 3D RoPE + block means call on each shape's Q/K projections (the
     pages' fused-kernel item): ms per call and HBM GB/s against the 8 TB/s peak for one
@@ -201,12 +225,17 @@ def norm_rope(args):
         both_ms = ev[1].elapsed_time(ev[2]) / reps
         nbytes = 2 * B * S * H * D * 2 + H * D * 2 + B * H * n * D * 4
         gbs = nbytes / (one_ms * 1e-3) / 1e9
+        cpu = None
+        if not args.no_cpu_baseline and name == "720p":
+            cpu = norm_rope_cpu_baseline(cfg)
         line = {
             "workload": "norm_rope %s: B=%d H=%d S=%d D=%d grid=%dx%dx%d block=%d" % ((name, B, H, S, D) + tuple(grid) + (block,)),
             "norm_rope_ms": round(one_ms, 4), "bytes": nbytes, "gb_per_s": round(gbs, 1),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "norm_rope_select_ms": round(both_ms, 4), "keep_ratio": cfg["keep_ratio"],
         }
+        if cpu is not None:
+            line["cpu_baseline"] = cpu
         print(json.dumps(line), flush=True)
         del xqd, xkd, out, xbar, ws, ws2
         torch.cuda.empty_cache()

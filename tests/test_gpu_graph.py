@@ -88,3 +88,33 @@ def test_fp8_steps_in_a_graph():
             torch.cuda.synchronize()
             assert torch.equal(eager[-1], ref[-1])
     assert np.isfinite(ref[-1].float().cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("H", [4, 40])
+def test_norm_rope_select_in_a_graph(H):
+    """The fused RMSNorm + 3D RoPE + selection call and the forward on its outputs, captured
+    and replayed (H = 40 takes the kernel's large-LDS launch)."""
+    B, D, block, r, grid = 1, 128, 128, 0.3, (4, 8, 12)
+    S = 4 * 8 * 12
+    xq, xk = gen.make_projections(B, S, H, D, 51, grid=grid, alpha=0.5)
+    wq, wk = gen.make_norm_weight(H * D, 52), gen.make_norm_weight(H * D, 53)
+    _, _, v = gen.make_qkv(B, H, S, D, 54)
+    xqd, xkd, wqd, wkd, vd = to_dev(xq), to_dev(xk), to_dev(wq), to_dev(wk), to_dev(v)
+
+    def step():
+        q, k, rp, ci = bsa.bsa_norm_rope_select(xqd, xkd, wqd, wkd, block, grid, r)
+        return q, k, rp, ci, bsa.bsa_forward(q, k, vd, block, rp, ci)
+
+    ref = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    g, outs = capture(step)
+    for _ in range(3):
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got, want)
+        eager = step()
+        torch.cuda.synchronize()
+        assert torch.equal(eager[-1], ref[-1])
