@@ -188,8 +188,10 @@ __global__ void __launch_bounds__(kNrThreads) norm_rope_kernel(const NormRopeArg
                 *(f32x4*)(mine + 8 * ci + 4) = s1;
             }
         }
+        if (tl + kNrWaves < tcount) {
 #pragma unroll
-        for (int k = 0; k < NCH; ++k) xv[k] = xn[k];
+            for (int k = 0; k < NCH; ++k) xv[k] = xn[k];
+        }
     }
 
     if (!a.partial) return;
