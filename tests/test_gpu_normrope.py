@@ -157,12 +157,14 @@ def test_norm_rope_select_small():
     assert float(same.float().mean()) >= 0.99  # fp32 pooling order differs: only near ties may move
 
 
-def test_norm_rope_select_720p_full_size():
-    """The 720p workload's shape (B=1, H=40, S=75600 on a 21x45x80 grid, D=128, block 128,
-    keep 0.15): every output element and every list against the oracle."""
-    cfg = gen.CONFIGS["720p"]
+@pytest.mark.parametrize("name", ["480p", "720p", "long"])
+def test_norm_rope_select_full_size(name):
+    """The workloads' shapes (B=1, H=40, D=128, block 128; 480p 21x30x52, 720p 21x45x80,
+    long 30x64x64 latent grids with their keep ratios): every output element and every list
+    against the oracle."""
+    cfg = gen.CONFIGS[name]
     out = run_select_case(cfg["B"], cfg["grid"], cfg["H"], cfg["D"], cfg["block"], cfg["keep_ratio"], 31)
-    print("720p: differing bits q %.2e k %.2e; lists: %d rows exact, %d near ties" % out[-1])
+    print("%s: differing bits q %.2e k %.2e; lists: %d rows exact, %d near ties" % ((name,) + out[-1]))
     del out
     gc.collect()
     torch.cuda.empty_cache()
