@@ -248,3 +248,29 @@ def test_norm_rope_select_rejects_bad_arguments(args, status):
                                     a["gt"], a["gh"], a["gw"], a["eps"], a["theta"], a["r"], a["q_out"], a["k_out"],
                                     a["rp"], a["ci"], a["ws"], a["ws_bytes"], None)
     assert st == status, bsa.bsa_last_error()
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """With libbsa.so absent the package raises ImportError on first use: there is no CPU or
+    PyTorch fallback."""
+    import subprocess
+    import sys
+
+    pkg = os.path.join(ROOT, "dynamic_block_sparse_bsa_amd", "__init__.py")
+    code = ("import importlib.util, sys\n"
+            "spec = importlib.util.spec_from_file_location('bsa_copy', %r)\n"
+            "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m)\n"
+            "m.lib_path = %r\n"
+            "try:\n    m.bsa_num_blocks(10, 4)\nexcept ImportError as e:\n    print('IMPORT_ERROR', e); sys.exit(0)\n"
+            "sys.exit(1)\n") % (pkg, str(tmp_path / "missing" / "libbsa.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "IMPORT_ERROR" in r.stdout, r.stdout + r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
