@@ -408,3 +408,34 @@ def test_large_magnitude_inputs_bf16_bar_scales_with_output(i):
     mx, mean = errors(got, exact)
     assert mean <= 1.25 * rounding.mean() + 1e-4, (mean, rounding.mean())
     assert mx <= 2.0 * rounding.max() + 1e-3, (mx, rounding.max())
+
+
+def test_every_path_repeats_bit_for_bit():
+    """No output depends on the order in which workgroups run: each call, made twice on the same
+    inputs, writes the same bits (selection, bf16, fp8-QK, full fp8, fused RMSNorm + RoPE)."""
+    B, H, S, D, block, r = 1, 3, 1100, 128, 128, 0.3
+    q, k, v = gen.make_qkv(B, H, S, D, 61, grid=(11, 10, 10), alpha=0.5)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    grid = (11, 10, 10)
+    xq, xk = gen.make_projections(B, S, H, D, 62, grid=grid, alpha=0.5)
+    wq, wk = to_dev(gen.make_norm_weight(H * D, 63)), to_dev(gen.make_norm_weight(H * D, 64))
+    xqd, xkd = to_dev(xq), to_dev(xk)
+
+    def run():
+        rp, ci = bsa.bsa_select(qd, kd, block, r)
+        o = bsa.bsa_forward(qd, kd, vd, block, rp, ci)
+        q8, qs = bsa.bsa_quantize_fp8(qd, block)
+        k8, ks = bsa.bsa_quantize_fp8(kd, block)
+        o8 = bsa.bsa_forward_fp8(q8, qs, k8, ks, vd, block, rp, ci)
+        rpf, cif, qf8, qfs, kf8, kfs = bsa.bsa_select_quantize(qd, kd, block, r)
+        vt8, vs = bsa.bsa_quantize_v_fp8(vd, block)
+        of = bsa.bsa_forward_fp8_full(qf8, qfs, kf8, kfs, vt8, vs, block, rpf, cif)
+        qn, xbar = bsa.bsa_norm_rope(xqd, wq, block, grid)
+        qs2, ks2, rpn, cin = bsa.bsa_norm_rope_select(xqd, xkd, wq, wk, block, grid, r)
+        torch.cuda.synchronize()
+        return [rp, ci, o, q8, qs, o8, qf8, vt8, vs, of, qn, xbar, qs2, ks2, rpn, cin]
+
+    first = [t.clone() for t in run()]
+    second = run()
+    for a_, b_ in zip(first, second):
+        assert torch.equal(a_, b_)
