@@ -75,9 +75,15 @@ def cpu_baseline(q, k, v, cfg, budget_tokens):
     oracle.attention(q, k, v, cfg["block"], ref["row_ptr"], ref["col_idx"], tokens=tok)
     t_att = time.perf_counter() - t0
     total_s = t_sel + t_att * (B * H * S) / budget_tokens
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": round(total_s * 1e3, 1), "unit": "ms/step", "cores": int(os.environ["OMP_NUM_THREADS"]),
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": model,
         "sample": "full selection (%.2f s) + attention for %d of %d query rows (%.2f s), scaled to all rows"
                   % (t_sel, budget_tokens, B * H * S, t_att),
     }
@@ -418,8 +424,10 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    sel_each = [e[0].elapsed_time(e[1]) for e in events]
+    fwd_each = [e[1].elapsed_time(e[2]) for e in events]
+    sel_ms = float(np.mean(sel_each))
+    fwd_ms = float(np.mean(fwd_each))
     step_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in events]))
 
     flop = 4.0 * D * kept_flops(rp.cpu().numpy(), ci.cpu().numpy(), S, block)
@@ -518,7 +526,11 @@ def main():
                    "global_batch": B, "seq_len": S, "heads": H, "head_dim": D, "block": block,
                    "keep_ratio": r, "parallelism": "single GPU"},
         "attention_ms": round(fwd_ms, 4),
+        "attention_ms_median": round(float(np.median(fwd_each)), 4),
+        "attention_ms_min": round(float(np.min(fwd_each)), 4),
         "select_ms": round(sel_ms, 4),
+        "select_ms_median": round(float(np.median(sel_each)), 4),
+        "select_ms_min": round(float(np.min(sel_each)), 4),
         "wall_ms_per_step": round(wall_ms, 4),
         "kept_tflop_per_call": round(flop / 1e12, 4),
         "kept_tflops": round(fwd_tflops, 1),
@@ -531,7 +543,8 @@ def main():
                      "kernel": "attn_kernel<128,128,bf16>"},
         "fp8_qk": {"quantize_ms": round(quant_ms, 4), "attention_ms": round(fwd8_ms, 4),
                    "kept_tflops": round(flop / (fwd8_ms * 1e-3) / 1e12, 1),
-                   "frac_mixed_peak": round(flop / (fwd8_ms * 1e-3) / 1e12 / (2 / (1 / FP8_PEAK_TFLOPS + 1 / BF16_PEAK_TFLOPS)), 4)},
+                   "frac_mixed_peak": round(flop / (fwd8_ms * 1e-3) / 1e12 / (2 / (1 / FP8_PEAK_TFLOPS + 1 / BF16_PEAK_TFLOPS)), 4),
+                   "frac_bf16_peak": round(flop / (fwd8_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "fp8_full": {"select_quantize_ms": round(selq_ms, 4), "quantize_v_ms": round(vq_ms, 4),
                      "attention_ms": round(fwdf_ms, 4),
                      "kept_tflops": round(flop / (fwdf_ms * 1e-3) / 1e12, 1),
