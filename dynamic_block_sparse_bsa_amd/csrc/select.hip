@@ -73,7 +73,7 @@ template <int D, int R>
 __global__ void __launch_bounds__(kThreads) select_kernel(const float* __restrict__ qbar, const float* __restrict__ kbarT,
                                                           int BH, int n, int kept, float scale,
                                                           int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
-    extern __shared__ float smem[];
+    extern __shared__ __attribute__((aligned(16))) float smem[];
     float* qs = smem;            // [R][D]
     float* sc = smem + R * D;    // [R][n]
     const int groups = (n + R - 1) / R;
@@ -86,15 +86,31 @@ __global__ void __launch_bounds__(kThreads) select_kernel(const float* __restric
     }
     __syncthreads();
 
-    const float* kb = kbarT + (int64_t)bh * D * n;
+    // K-bar^T of this head through a buffer resource: the channel offset is a scalar, so the
+    // 16 loads a thread keeps in flight per batch cost no per-lane address arithmetic. Each
+    // score still adds its D products in channel order.
+    const __amdgpu_buffer_rsrc_t kb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(kbarT + (int64_t)bh * D * n), 0, D * n * 4, 0x00020000);
+    constexpr int DB = 16;  // channels per batch of loads
     for (int j = threadIdx.x; j < n; j += kThreads) {
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-        for (int d = 0; d < D; ++d) {
-            const float kv = kb[(int64_t)d * n + j];
+        for (int d0 = 0; d0 < D; d0 += DB) {
+            float kv[DB];
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(qs[r * D + d], kv, acc[r]);
+            for (int u = 0; u < DB; ++u)
+                kv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kb, j * 4, (d0 + u) * n * 4, 0));
+#pragma unroll
+            for (int u = 0; u < DB; u += 4)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const f32x4 qv = *(const f32x4*)(qs + r * D + d0 + u);
+                    acc[r] = __builtin_fmaf(qv[0], kv[u], acc[r]);
+                    acc[r] = __builtin_fmaf(qv[1], kv[u + 1], acc[r]);
+                    acc[r] = __builtin_fmaf(qv[2], kv[u + 2], acc[r]);
+                    acc[r] = __builtin_fmaf(qv[3], kv[u + 3], acc[r]);
+                }
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) sc[r * n + j] = acc[r] * scale;
