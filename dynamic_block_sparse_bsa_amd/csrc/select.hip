@@ -42,12 +42,22 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(const uint16_t* __restri
     const int c = threadIdx.x % CH, tl = threadIdx.x / CH;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const uint16_t* base = x + ((int64_t)bh * S + t0) * D + 8 * c;
-    for (int t = tl; t < cnt; t += TL) {
-        u32x4 w = *(const u32x4*)(base + (int64_t)t * D);
+    // All of a thread's loads (blocks hold at most 128 tokens) are issued before the first
+    // sum; the sums still run over the tokens in ascending order.
+    constexpr int MAXT = 128 / TL;
+    u32x4 w[MAXT];
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+        const int t = tl + u * TL;
+        w[u] = t < cnt ? *(const u32x4*)(base + (int64_t)t * D) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+        if (tl + u * TL >= cnt) break;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += __uint_as_float(w[e] << 16);
-            acc[2 * e + 1] += __uint_as_float(w[e] & 0xFFFF0000u);
+            acc[2 * e] += __uint_as_float(w[u][e] << 16);
+            acc[2 * e + 1] += __uint_as_float(w[u][e] & 0xFFFF0000u);
         }
     }
 #pragma unroll
