@@ -30,9 +30,35 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
-        _build.build()
-    lib = ctypes.CDLL(_build.LIB)
+    path = os.environ.get("BSA_ORACLE_LIB")  # another build of bsa_oracle.c (mutation tests)
+    if not path:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+    _lib = _bind(ctypes.CDLL(path))
+    return _lib
+
+
+class use_library:
+    """Context manager: route every call of this module to another build of bsa_oracle.c
+    (the mutation tests load deliberately broken copies through it)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _load()
+        _lib = _bind(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def _bind(lib):
     P = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     lib.oracle_num_blocks.restype = i32
@@ -57,13 +83,14 @@ def _load():
     lib.oracle_attention_fp8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, i64, P]
     lib.oracle_quantize_v_fp8.restype = None
     lib.oracle_quantize_v_fp8.argtypes = [P, i32, i32, i32, i32, P, P]
+    lib.oracle_attention_fp8_qkv.restype = None
+    lib.oracle_attention_fp8_qkv.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, i64, P, P]
     lib.oracle_attention_fp8_full.restype = None
     lib.oracle_attention_fp8_full.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, i64, P]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
     lib.oracle_round_bf16.argtypes = [f64]
     lib.oracle_norm_rope.restype = None
     lib.oracle_norm_rope.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, f64, f64, P, P]
-    _lib = lib
     return lib
 
 
@@ -231,6 +258,40 @@ def quantize_v_fp8(v):
     scale = np.empty((B, H, D), dtype=np.float32)
     _load().oracle_quantize_v_fp8(_ptr(v), B, H, S, D, _ptr(codes), _ptr(scale))
     return codes, scale
+
+
+def attention_fp8_qkv(q8, q_scale, k8, k_scale, v8, v_scale, block: int, row_ptr, col_idx, tokens=None,
+                      spread=False):
+    """Exact (fp64) attention over the full FP8 path's dequantised operands: Q, K with
+    per-block scales, V with per-channel scales (codes in the [B, H, S, D] layout of
+    quantize_v_fp8); the softmax weights are not rounded. With spread=True also returns
+    dev [..., 3, D]: sum_u p_u |v_u - o|, sum_u |v_u - o| and sqrt(sum_u p_u^2 (v_u - o)^2)."""
+    q8 = np.ascontiguousarray(q8, dtype=np.uint8)
+    k8 = np.ascontiguousarray(k8, dtype=np.uint8)
+    v8 = np.ascontiguousarray(v8, dtype=np.uint8)
+    if q8.ndim != 4 or k8.shape != q8.shape or v8.shape != q8.shape:
+        raise ValueError("fp8 operand shapes do not match")
+    B, H, S, D = q8.shape
+    n = num_blocks(S, block)
+    q_scale = np.ascontiguousarray(q_scale, dtype=np.float32)
+    k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+    v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+    if q_scale.size != B * H * n or k_scale.size != B * H * n or v_scale.size != B * H * D:
+        raise ValueError("scale shapes do not match")
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
+    check_csr(row_ptr, col_idx, B * H * n, n)
+    t, nt = _tokens_arg(tokens)
+    rows = (B * H * S) if t is None else nt
+    out = np.empty((rows, D), dtype=np.float64)
+    dev = np.empty((rows, 3, D), dtype=np.float64) if spread else None
+    _load().oracle_attention_fp8_qkv(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale),
+                                     B, H, S, D, block, _ptr(row_ptr), _ptr(col_idx), _ptr(t), nt, _ptr(out),
+                                     _ptr(dev))
+    if t is None:
+        out = out.reshape(B, H, S, D)
+        dev = dev.reshape(B, H, S, 3, D) if spread else None
+    return (out, dev) if spread else out
 
 
 def attention_fp8_full(q8, q_scale, k8, k_scale, v8, v_scale, block: int, row_ptr, col_idx, tokens=None):

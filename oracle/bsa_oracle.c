@@ -33,7 +33,11 @@
  *     sequence; the softmax runs online over the kept keys in list order, 64 keys at a
  *     time, and each 64-key sub-tile's weights 2^(x - m) <= 1 (x the logit in log2 units,
  *     m the running maximum after that sub-tile) are stored as E4M3FN codes of 448 times
- *     the weight; the normaliser is the sum of the stored weights.
+ *     the weight; the normaliser is the sum of the stored weights. That sub-tile schedule
+ *     is one kernel's order of work, so it serves as a diagnostic; the full FP8 path is
+ *     graded against oracle_attention_fp8_qkv (exact softmax over the dequantised Q, K and
+ *     V) with a bound on what rounding the weights to E4M3 can change, which holds for any
+ *     order and reference point.
  *
  * Layouts: tensors are [B, H, S, D] row-major; bf16 values are passed as their raw
  * 16-bit patterns. Block i of a sequence is tokens [i*block, min(S,(i+1)*block)).
@@ -88,18 +92,21 @@ uint8_t oracle_e4m3_encode(double x) {
 }
 
 /* A tensor as the attention definition reads it: either bf16 bits, or E4M3 codes with
- * one scale per (batch*head, block). */
+ * one scale per (batch*head, block), or (chan_scale) one scale per (batch*head, channel). */
 typedef struct {
     const uint16_t* bf16;
     const uint8_t* e4m3;
     const float* scale;
+    const float* chan_scale;
     int64_t S, D, block, nblk;
 } tensor_t;
 
 static double load(const tensor_t* T, int64_t bh, int64_t t, int64_t d) {
     int64_t off = (bh * T->S + t) * T->D + d;
     if (T->bf16) return bf16_value(T->bf16[off]);
-    return oracle_e4m3_value(T->e4m3[off]) * (double)T->scale[bh * T->nblk + t / T->block];
+    double sc = T->chan_scale ? (double)T->chan_scale[bh * T->D + d]
+                              : (double)T->scale[bh * T->nblk + t / T->block];
+    return oracle_e4m3_value(T->e4m3[off]) * sc;
 }
 
 /* ---- block partition and the k rule ----------------------------------------------- */
@@ -194,10 +201,13 @@ void oracle_select(const double* s, int32_t rows, int32_t n, int32_t k, int32_t*
 
 /* For every requested query token, softmax(Q_t K_u^T / sqrt(D)) V_u over the keys u of
  * the kept blocks of t's block ([AO] 动态稀疏注意力: dense inside the selected blocks).
- * tokens[m] = bh*S + t; NULL means all B*H*S tokens in order. out is [ntok, D]. */
+ * tokens[m] = bh*S + t; NULL means all B*H*S tokens in order. out is [ntok, D].
+ * dev (optional, [ntok, 3, D]) receives, per output element, the spread of the values
+ * around it: sum_u p_u |v_ud - o_d|, sum_u |v_ud - o_d| and sqrt(sum_u p_u^2 (v_ud - o_d)^2)
+ * (p the softmax weights); the full FP8 path's error bound is built from them. */
 static void attention_core(const tensor_t* Q, const tensor_t* K, const tensor_t* V, int64_t BH,
                            const int32_t* row_ptr, const int32_t* col_idx,
-                           const int64_t* tokens, int64_t ntok, double* out) {
+                           const int64_t* tokens, int64_t ntok, double* out, double* dev) {
     int64_t S = Q->S, D = Q->D, block = Q->block, n = Q->nblk;
     double inv = 1.0 / sqrt((double)D);
     (void)BH;
@@ -231,6 +241,20 @@ static void attention_core(const tensor_t* Q, const tensor_t* K, const tensor_t*
                 double p = logit[a] / denom;
                 for (int64_t d = 0; d < D; ++d) o[d] += p * load(V, bh, key[a], d);
             }
+            if (dev) {
+                double* dv = dev + m * 3 * D;
+                for (int64_t d = 0; d < 3 * D; ++d) dv[d] = 0.0;
+                for (int64_t a = 0; a < nk; ++a) {
+                    double p = logit[a] / denom;
+                    for (int64_t d = 0; d < D; ++d) {
+                        double e = fabs(load(V, bh, key[a], d) - o[d]);
+                        dv[d] += p * e;
+                        dv[D + d] += e;
+                        dv[2 * D + d] += p * p * e * e;
+                    }
+                }
+                for (int64_t d = 0; d < D; ++d) dv[2 * D + d] = sqrt(dv[2 * D + d]);
+            }
         }
         free(logit); free(key); free(qrow);
     }
@@ -240,10 +264,10 @@ void oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
                       int32_t H, int32_t S, int32_t D, int32_t block, const int32_t* row_ptr,
                       const int32_t* col_idx, const int64_t* tokens, int64_t ntok, double* out) {
     int64_t n = oracle_num_blocks(S, block);
-    tensor_t Q = {q, NULL, NULL, S, D, block, n}, K = {k, NULL, NULL, S, D, block, n},
-             V = {v, NULL, NULL, S, D, block, n};
+    tensor_t Q = {q, NULL, NULL, NULL, S, D, block, n}, K = {k, NULL, NULL, NULL, S, D, block, n},
+             V = {v, NULL, NULL, NULL, S, D, block, n};
     if (!tokens) ntok = (int64_t)B * H * S;
-    attention_core(&Q, &K, &V, (int64_t)B * H, row_ptr, col_idx, tokens, ntok, out);
+    attention_core(&Q, &K, &V, (int64_t)B * H, row_ptr, col_idx, tokens, ntok, out, NULL);
 }
 
 /* ---- FP8 path ([KC] 动态稀疏量化注意力: SageAttention2 FP8 sparse path) ------------ */
@@ -279,10 +303,10 @@ void oracle_attention_fp8(const uint8_t* q8, const float* q_scale, const uint8_t
                           const int32_t* col_idx, const int64_t* tokens, int64_t ntok,
                           double* out) {
     int64_t n = oracle_num_blocks(S, block);
-    tensor_t Q = {NULL, q8, q_scale, S, D, block, n}, K = {NULL, k8, k_scale, S, D, block, n},
-             V = {v, NULL, NULL, S, D, block, n};
+    tensor_t Q = {NULL, q8, q_scale, NULL, S, D, block, n}, K = {NULL, k8, k_scale, NULL, S, D, block, n},
+             V = {v, NULL, NULL, NULL, S, D, block, n};
     if (!tokens) ntok = (int64_t)B * H * S;
-    attention_core(&Q, &K, &V, (int64_t)B * H, row_ptr, col_idx, tokens, ntok, out);
+    attention_core(&Q, &K, &V, (int64_t)B * H, row_ptr, col_idx, tokens, ntok, out, NULL);
 }
 
 /* ---- Full FP8 path: P and V in E4M3 as well -------------------------------------------
@@ -312,6 +336,25 @@ void oracle_quantize_v_fp8(const uint16_t* v, int32_t B, int32_t H, int32_t S, i
             codes[off] = oracle_e4m3_encode((double)y);
         }
     }
+}
+
+/* The full FP8 path's operands without its weight rounding: exact softmax attention (fp64)
+ * over Q and K dequantised from E4M3 codes with their per-(batch*head, block) scales and V
+ * dequantised with its per-(batch*head, channel) scales. Rounding the softmax weights to
+ * E4M3 moves each weight by at most 2^-4 of itself (or by an absolute amount below the
+ * smallest subnormal step, for weights in the subnormal range), whatever the order in which a
+ * kernel visits the keys and wherever it takes its reference point, so this result together
+ * with the spread terms in dev bounds every such kernel. dev as in attention_core. */
+void oracle_attention_fp8_qkv(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                              const float* k_scale, const uint8_t* v8, const float* v_scale,
+                              int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                              const int32_t* row_ptr, const int32_t* col_idx,
+                              const int64_t* tokens, int64_t ntok, double* out, double* dev) {
+    int64_t n = oracle_num_blocks(S, block);
+    tensor_t Q = {NULL, q8, q_scale, NULL, S, D, block, n}, K = {NULL, k8, k_scale, NULL, S, D, block, n},
+             V = {NULL, v8, NULL, v_scale, S, D, block, n};
+    if (!tokens) ntok = (int64_t)B * H * S;
+    attention_core(&Q, &K, &V, (int64_t)B * H, row_ptr, col_idx, tokens, ntok, out, dev);
 }
 
 /* Attention with Q, K (per-block scales) and V (per-channel scales) as E4M3 codes and the

@@ -10,14 +10,15 @@ SRC = os.path.join(HERE, "bsa_oracle.c")
 LIB = os.path.join(HERE, "libbsa_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, src: str = SRC, lib: str = LIB) -> str:
+    """Compile src (the oracle, or a copy of it) into the shared library lib."""
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-Wall", "-Wextra", "-shared", "-fPIC",
-           SRC, "-o", LIB + ".tmp", "-lm"]
+           src, "-o", lib + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -369,6 +369,111 @@ def test_fp8_exact_inputs_reduce_to_bf16_attention():
     assert np.max(np.abs(a - b)) <= 1e-13
 
 
+def random_e4m3_codes(rng, shape):
+    """Uniform over the 254 finite E4M3FN codes (both NaN patterns excluded)."""
+    c = rng.integers(0, 254, size=shape).astype(np.uint8)
+    return np.where(c >= 0x7F, c + 1, c).astype(np.uint8)  # skip 0x7F; 0xFF is never drawn
+
+
+def dequant_torch(codes, scale_rows):
+    """Library decode of E4M3FN codes (torch's float8_e4m3fn) times a broadcast scale."""
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale_rows
+
+
+def block_scales_to_tokens(scale, S, block):
+    """[B, H, n] per-block scales -> [B, H, S, 1] per-token scales."""
+    return np.repeat(scale.astype(np.float64), block, axis=2)[:, :, :S, None]
+
+
+def sdpa_f64_values(q, k, v, mask):
+    t = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64)) for x in (q, k, v)]
+    return torch.nn.functional.scaled_dot_product_attention(t[0], t[1], t[2], attn_mask=torch.from_numpy(mask)).numpy()
+
+
+def random_lists(rng, B, H, n, k):
+    rows = B * H * n
+    col = np.concatenate([np.sort(rng.choice(n, size=k, replace=False)) for _ in range(rows)]).astype(np.int32)
+    return (np.arange(rows + 1) * k).astype(np.int32), col
+
+
+def check_fp8_qk_random_scales():
+    """attention_fp8 on random E4M3 codes with random per-block scales (different for Q and
+    K, spread over four binades) equals library attention on the values dequantised by
+    torch's float8_e4m3fn decode and the scales repeated over each block's tokens."""
+    B, H, S, D, block = 1, 3, 200, 16, 64
+    rng = np.random.default_rng(91)
+    n = oracle.num_blocks(S, block)
+    q8 = random_e4m3_codes(rng, (B, H, S, D))
+    k8 = random_e4m3_codes(rng, (B, H, S, D))
+    qs = np.exp2(rng.uniform(-12, -8, size=(B, H, n))).astype(np.float32)
+    ks = np.exp2(rng.uniform(-12, -8, size=(B, H, n))).astype(np.float32)
+    _, _, v = gen.make_qkv(B, H, S, D, 92)
+    rp, ci = random_lists(rng, B, H, n, 2)
+    got = oracle.attention_fp8(q8, qs, k8, ks, v, block, rp, ci)
+    qv = dequant_torch(q8, block_scales_to_tokens(qs, S, block))
+    kv = dequant_torch(k8, block_scales_to_tokens(ks, S, block))
+    want = sdpa_f64_values(qv, kv, f32(v).astype(np.float64), lists_to_mask(rp, ci, B, H, S, block))
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+def test_fp8_qk_random_scales_equal_library_attention_on_dequantised_operands():
+    check_fp8_qk_random_scales()
+
+
+def check_fp8_qkv_random_scales():
+    """attention_fp8_qkv (the full FP8 path's operands, exact softmax) on random codes with
+    random per-block Q/K scales and per-channel V scales equals library attention on the
+    torch-decoded values; its spread terms equal a direct evaluation from the library's
+    softmax weights."""
+    B, H, S, D, block = 1, 2, 190, 16, 64
+    rng = np.random.default_rng(93)
+    n = oracle.num_blocks(S, block)
+    q8, k8, v8 = (random_e4m3_codes(rng, (B, H, S, D)) for _ in range(3))
+    qs = np.exp2(rng.uniform(-12, -8, size=(B, H, n))).astype(np.float32)
+    ks = np.exp2(rng.uniform(-12, -8, size=(B, H, n))).astype(np.float32)
+    vs = np.exp2(rng.uniform(-9, -5, size=(B, H, D))).astype(np.float32)
+    rp, ci = random_lists(rng, B, H, n, 2)
+    got, dev = oracle.attention_fp8_qkv(q8, qs, k8, ks, v8, vs, block, rp, ci, spread=True)
+    qv = dequant_torch(q8, block_scales_to_tokens(qs, S, block))
+    kv = dequant_torch(k8, block_scales_to_tokens(ks, S, block))
+    vv = dequant_torch(v8, vs.astype(np.float64)[:, :, None, :])
+    mask = lists_to_mask(rp, ci, B, H, S, block)
+    want = sdpa_f64_values(qv, kv, vv, mask)
+    assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.abs(want).max())
+    logits = torch.from_numpy(qv) @ torch.from_numpy(kv).transpose(-1, -2) / math.sqrt(D)
+    p = torch.softmax(logits.masked_fill(~torch.from_numpy(mask), float("-inf")), dim=-1).numpy()
+    e = np.abs(vv[:, :, None, :, :] - want[:, :, :, None, :])       # [B, H, S(query), S(key), D]
+    on = mask[..., None]
+    a = np.sum(p[..., None] * e, axis=3)
+    b = np.sum(np.where(on, e, 0.0), axis=3)
+    r = np.sqrt(np.sum((p[..., None] * e) ** 2, axis=3))
+    assert np.allclose(dev[..., 0, :], a, rtol=1e-10, atol=1e-14)
+    assert np.allclose(dev[..., 1, :], b, rtol=1e-10, atol=1e-14)
+    assert np.allclose(dev[..., 2, :], r, rtol=1e-10, atol=1e-14)
+
+
+def test_fp8_qkv_random_scales_equal_library_attention_on_dequantised_operands():
+    check_fp8_qkv_random_scales()
+
+
+def test_fp8_qkv_with_unit_scales_equals_the_bf16_definition():
+    # E4M3 values of magnitude <= 2 are bf16-exact; with every scale 1 the three operands
+    # are the same numbers as their bf16 patterns, so the result is oracle.attention's.
+    B, H, S, D, block = 1, 2, 256, 16, 64
+    rng = np.random.default_rng(94)
+    n = oracle.num_blocks(S, block)
+    codes = [random_e4m3_codes(rng, (B, H, S, D)) & np.uint8(0xBF) for _ in range(3)]  # exponent <= 7: |x| < 2
+    vals = [dequant_torch(c, 1.0) for c in codes]
+    bits = [bf16(x.astype(np.float32)) for x in vals]
+    assert all(np.array_equal(f32(b_), x) for b_, x in zip(bits, vals))
+    sel = oracle.select(bits[0], bits[1], block, 0.5)
+    one_n = np.ones((B, H, n), np.float32)
+    got = oracle.attention_fp8_qkv(codes[0], one_n, codes[1], one_n, codes[2], np.ones((B, H, D), np.float32), block,
+                                   sel["row_ptr"], sel["col_idx"])
+    want = oracle.attention(bits[0], bits[1], bits[2], block, sel["row_ptr"], sel["col_idx"])
+    assert np.max(np.abs(got - want)) <= 1e-13
+
+
 # ---- full FP8 path: P and V in E4M3 as well --------------------------------------------
 
 def e4m3_round(x):
