@@ -102,6 +102,31 @@ def _dev_tensor(t, name, dtypes, ndim=4):
 _ONE_BYTE = (torch.uint8, torch.int8, torch.float8_e4m3fn)
 
 
+def _given(t, name, dtypes, numel, device, shape=None):
+    """Checks a caller-provided output or buffer before any launch: a contiguous tensor on
+    `device` of one of `dtypes` with exactly `numel` elements (and `shape`, if given)."""
+    _dev_tensor(t, name, dtypes, ndim=None)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.numel() != numel:
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
+    return t
+
+
+def _bytes_at_least(t, name, nbytes, device):
+    """A caller's scratch buffer: any dtype, contiguous, on `device`, at least nbytes."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    _dev_tensor(t, name, (t.dtype,), ndim=None)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes, needs %d" % (name, t.numel() * t.element_size(), nbytes))
+    return t
+
+
 def _p(t):
     return ctypes.c_void_p(t.data_ptr())
 
@@ -125,6 +150,7 @@ def bsa_pool(x, block: int, out=None):
     n = bsa_num_blocks(S, block)
     if out is None:
         out = torch.empty((B, H, n, D), dtype=torch.float32, device=x.device)
+    _given(out, "out", (torch.float32,), B * H * n * D, x.device)
     _check(_load().bsa_pool(_p(x), B, H, S, D, block, _p(out), _stream(x)))
     return out
 
@@ -148,16 +174,23 @@ def bsa_select(q, k, block: int, keep_ratio: float, workspace=None, row_ptr=None
         row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
     if col_idx is None:
         col_idx = torch.empty(rows * kept, dtype=torch.int32, device=q.device)
+    _bytes_at_least(workspace, "workspace", ws_bytes, q.device)
+    _given(row_ptr, "row_ptr", (torch.int32,), rows + 1, q.device)
+    _given(col_idx, "col_idx", (torch.int32,), rows * kept, q.device)
     _check(_load().bsa_select(_p(q), _p(k), B, H, S, D, block, keep_ratio, _p(row_ptr), _p(col_idx),
                               _p(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
     return row_ptr, col_idx
 
 
-def _csr(row_ptr, col_idx, device):
+def _csr(row_ptr, col_idx, device, rows):
+    """Device CSR over `rows` query-block rows. col_idx must hold row_ptr[rows] entries; that
+    count lives on the device and is not read here (reading it would synchronise)."""
     for t, name in ((row_ptr, "row_ptr"), (col_idx, "col_idx")):
         _dev_tensor(t, name, (torch.int32,), ndim=1)
         if t.device != device:
             raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if row_ptr.numel() != rows + 1:
+        raise ValueError("row_ptr has %d entries, expected B*H*n + 1 = %d" % (row_ptr.numel(), rows + 1))
 
 
 def bsa_forward(q, k, v, block: int, row_ptr, col_idx, out=None):
@@ -166,11 +199,11 @@ def bsa_forward(q, k, v, block: int, row_ptr, col_idx, out=None):
         _dev_tensor(t, name, (torch.bfloat16,))
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k, v shapes differ")
-    _csr(row_ptr, col_idx, q.device)
     B, H, S, D = q.shape
+    _csr(row_ptr, col_idx, q.device, B * H * bsa_num_blocks(S, block))
     if out is None:
         out = torch.empty_like(q)
-    _dev_tensor(out, "out", (torch.bfloat16,))
+    _given(out, "out", (torch.bfloat16,), q.numel(), q.device, shape=q.shape)
     _check(_load().bsa_forward(_p(q), _p(k), _p(v), B, H, S, D, block, _p(row_ptr), _p(col_idx), _p(out),
                                _stream(q)))
     return out
@@ -185,6 +218,8 @@ def bsa_quantize_fp8(x, block: int, codes=None, scale=None):
         codes = torch.empty((B, H, S, D), dtype=torch.uint8, device=x.device)
     if scale is None:
         scale = torch.empty((B, H, n), dtype=torch.float32, device=x.device)
+    _given(codes, "codes", _ONE_BYTE, x.numel(), x.device)
+    _given(scale, "scale", (torch.float32,), B * H * n, x.device)
     _check(_load().bsa_quantize_fp8(_p(x), B, H, S, D, block, _p(codes), _p(scale), _stream(x)))
     return codes, scale
 
@@ -202,10 +237,13 @@ def bsa_forward_fp8(q8, q_scale, k8, k_scale, v, block: int, row_ptr, col_idx, o
         _dev_tensor(t, name, (torch.float32,), ndim=None)
         if t.numel() != B * H * n:
             raise ValueError("%s must have B*H*n = %d entries" % (name, B * H * n))
-    _csr(row_ptr, col_idx, v.device)
+    _csr(row_ptr, col_idx, v.device, B * H * n)
+    for t, name in ((q8, "q_e4m3"), (k8, "k_e4m3"), (q_scale, "q_scale"), (k_scale, "k_scale")):
+        if t.device != v.device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, v.device))
     if out is None:
         out = torch.empty_like(v)
-    _dev_tensor(out, "out", (torch.bfloat16,))
+    _given(out, "out", (torch.bfloat16,), v.numel(), v.device, shape=v.shape)
     _check(_load().bsa_forward_fp8(_p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(v), B, H, S, D, block,
                                    _p(row_ptr), _p(col_idx), _p(out), _stream(v)))
     return out
@@ -234,6 +272,9 @@ def bsa_select_quantize(q, k, block: int, keep_ratio: float, workspace=None, row
         row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
     if col_idx is None:
         col_idx = torch.empty(rows * kept, dtype=torch.int32, device=q.device)
+    _bytes_at_least(workspace, "workspace", bsa_select_workspace_bytes(B, H, S, D, block), q.device)
+    _given(row_ptr, "row_ptr", (torch.int32,), rows + 1, q.device)
+    _given(col_idx, "col_idx", (torch.int32,), rows * kept, q.device)
     q8 = torch.empty((B, H, S, D), dtype=torch.uint8, device=q.device)
     k8 = torch.empty_like(q8)
     qs = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
@@ -254,8 +295,8 @@ def bsa_quantize_v_fp8(v, block: int, vt=None, scale=None):
         vt = torch.empty((B * H, D, n * block), dtype=torch.uint8, device=v.device)
     if scale is None:
         scale = torch.empty((B, H, D), dtype=torch.float32, device=v.device)
-    if vt.numel() != bsa_vt_fp8_bytes(B, H, S, D, block):
-        raise ValueError("vt must hold bsa_vt_fp8_bytes bytes")
+    _given(vt, "vt", _ONE_BYTE, bsa_vt_fp8_bytes(B, H, S, D, block), v.device)
+    _given(scale, "scale", (torch.float32,), B * H * D, v.device)
     _check(_load().bsa_quantize_v_fp8(_p(v), B, H, S, D, block, _p(vt), _p(scale), _stream(v)))
     return vt, scale
 
@@ -275,10 +316,13 @@ def bsa_forward_fp8_full(q8, q_scale, k8, k_scale, vt8, v_scale, block: int, row
         _dev_tensor(t, name, (torch.float32,), ndim=None)
         if t.numel() != cnt:
             raise ValueError("%s must have %d entries" % (name, cnt))
-    _csr(row_ptr, col_idx, q8.device)
+    _csr(row_ptr, col_idx, q8.device, B * H * n)
+    for t, name in ((k8, "k_e4m3"), (vt8, "vt_e4m3"), (q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t.device != q8.device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, q8.device))
     if out is None:
         out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=q8.device)
-    _dev_tensor(out, "out", (torch.bfloat16,))
+    _given(out, "out", (torch.bfloat16,), B * H * S * D, q8.device, shape=(B, H, S, D))
     _check(_load().bsa_forward_fp8_full(_p(q8), _p(q_scale), _p(k8), _p(k_scale), _p(vt8), _p(v_scale), B, H, S, D,
                                         block, _p(row_ptr), _p(col_idx), _p(out), _stream(q8)))
     return out
@@ -332,20 +376,24 @@ def bsa_norm_rope(x, weight, block: int, grid, eps: float = 1e-6, theta: float =
     gt, gh, gw = (int(g) for g in grid)
     if out is None:
         out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=x.device)
+    _given(out, "out", (torch.bfloat16,), B * H * S * D, x.device, shape=(B, H, S, D))
     ws_bytes = 0
     if means:
         n = bsa_num_blocks(S, block)
         if xbar is None:
             xbar = torch.empty((B, H, n, D), dtype=torch.float32, device=x.device)
+        _given(xbar, "xbar", (torch.float32,), B * H * n * D, x.device)
         ws_bytes = bsa_norm_rope_workspace_bytes(B, H, S, D)
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+        _bytes_at_least(workspace, "workspace", ws_bytes, x.device)
     else:
         xbar = None
     _check(_load().bsa_norm_rope(_p(x), _p(weight), B, H, S, D, block, gt, gh, gw, float(eps), float(theta), _p(out),
                                  _p(xbar) if xbar is not None else None,
                                  _p(workspace) if workspace is not None else None,
-                                 workspace.numel() if workspace is not None else 0, _stream(x)))
+                                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                 _stream(x)))
     return out, xbar
 
 
@@ -369,7 +417,8 @@ def bsa_norm_rope_select(xq, xk, wq, wk, block: int, grid, keep_ratio: float, ep
     ws_bytes = bsa_norm_rope_select_workspace_bytes(B, H, S, D, block)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=xq.device)
+    _bytes_at_least(workspace, "workspace", ws_bytes, xq.device)
     _check(_load().bsa_norm_rope_select(_p(xq), _p(xk), _p(wq), _p(wk), B, H, S, D, block, gt, gh, gw, float(eps),
                                         float(theta), float(keep_ratio), _p(q), _p(k), _p(row_ptr), _p(col_idx),
-                                        _p(workspace), workspace.numel(), _stream(xq)))
+                                        _p(workspace), workspace.numel() * workspace.element_size(), _stream(xq)))
     return q, k, row_ptr, col_idx

@@ -478,8 +478,11 @@ attn_kernel(const AttnArgs a) {
         const int r = S - key0;
         return r < KT ? r : KT;
     };
-    auto block_scale = [&](int pp) -> float {  // logit scale of list entry pp (window current)
-        if constexpr (FP8) return qscale_log2 * entry_kscale(pp);
+    // Logit scale of list entry pp (window current). The fp8 product of two scales is kept at
+    // least FLT_MIN: masked keys are -inf before this scale is applied, and a zero scale (a
+    // caller's, or two tiny ones whose product underflows) would turn them into NaN.
+    auto block_scale = [&](int pp) -> float {
+        if constexpr (FP8) return fmaxf(qscale_log2 * entry_kscale(pp), 0x1p-126f);
         else return qscale_log2;
     };
     int pos = valid_block(p);

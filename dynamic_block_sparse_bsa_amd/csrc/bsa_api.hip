@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -92,6 +93,24 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
     return x < y + bn && y < x + an;
 }
 
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+// True when an output range overlaps an input range or another output range.
+bool outputs_overlap(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span& i : ins)
+            if (overlaps(o->p, o->bytes, i.p, i.bytes)) return true;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlaps(o->p, o->bytes, o2->p, o2->bytes)) return true;
+    }
+    return false;
+}
+
+size_t elems(int32_t B, int32_t H, int32_t S, int32_t D) { return (size_t)B * H * S * D; }
+
 // Checks shared by the fused RMSNorm + RoPE calls (one projection).
 bsa_status check_norm_rope(const void* x, const void* w, const void* out, int32_t B, int32_t H, int32_t S, int32_t D,
                            int32_t block, int32_t gt, int32_t gh, int32_t gw, double eps, double theta) {
@@ -158,6 +177,9 @@ bsa_status bsa_pool(const void* x, int32_t B, int32_t H, int32_t S, int32_t D, i
     if (st != BSA_OK) return st;
     if (!x || !xbar) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
     if (!aligned16(x) || !aligned16(xbar)) return fail(BSA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    const size_t n = (size_t)bsa_num_blocks(S, block);
+    if (outputs_overlap({{xbar, (size_t)B * H * n * D * 4}}, {{x, elems(B, H, S, D) * 2}}))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "xbar must not overlap x");
     if ((st = check_device()) != BSA_OK) return st;
     return hip_result(bsa::launch_pool(x, B * H, S, D, block, xbar, false, as_stream(hip_stream)), "pool launch");
 }
@@ -178,6 +200,9 @@ bsa_status bsa_select(const void* q, const void* k, int32_t B, int32_t H, int32_
     if ((int64_t)B * H * n * kept >= ((int64_t)1 << 31)) return fail(BSA_ERR_UNSUPPORTED, "kept-block list too long for int32 indices");
     const size_t need = bsa_select_workspace_bytes(B, H, S, D, block);
     if (workspace_bytes < need) return fail(BSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    const size_t rows = (size_t)B * H * n, tbytes = elems(B, H, S, D) * 2;
+    if (outputs_overlap({{row_ptr, (rows + 1) * 4}, {col_idx, rows * kept * 4}, {workspace, need}}, {{q, tbytes}, {k, tbytes}}))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr, col_idx and workspace must not overlap q, k or each other");
     if ((st = check_device()) != BSA_OK) return st;
     float* qbar = (float*)workspace;
     float* kbarT = qbar + (size_t)B * H * n * D;
@@ -199,7 +224,13 @@ static bsa_status forward_common(const void* q, const float* q_scale, const void
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
     if (((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u)) return fail(BSA_ERR_INVALID_ARGUMENT, "misaligned CSR arrays");
-    if (out == q || out == k || out == v) return fail(BSA_ERR_INVALID_ARGUMENT, "out must not alias an input");
+    {
+        const size_t e = elems(B, H, S, D), rows = (size_t)B * H * bsa_num_blocks(S, block);
+        const size_t qk_bytes = mode == 0 ? 2 * e : e;
+        const size_t v_bytes = mode == 2 ? bsa_vt_fp8_bytes(B, H, S, D, block) : 2 * e;
+        if (outputs_overlap({{out, 2 * e}}, {{q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {row_ptr, (rows + 1) * 4}}))
+            return fail(BSA_ERR_INVALID_ARGUMENT, "out must not overlap q, k, v or row_ptr");
+    }
     if ((st = check_device()) != BSA_OK) return st;
     bsa::AttnArgs a;
     a.q = q;
@@ -254,6 +285,13 @@ bsa_status bsa_select_quantize(const void* q, const void* k, int32_t B, int32_t 
     if ((int64_t)B * H * n * kept >= ((int64_t)1 << 31)) return fail(BSA_ERR_UNSUPPORTED, "kept-block list too long for int32 indices");
     const size_t need = bsa_select_workspace_bytes(B, H, S, D, block);
     if (workspace_bytes < need) return fail(BSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    {
+        const size_t rows = (size_t)B * H * n, e = elems(B, H, S, D);
+        if (outputs_overlap({{row_ptr, (rows + 1) * 4}, {col_idx, rows * kept * 4}, {workspace, need}, {q_e4m3, e},
+                             {k_e4m3, e}, {q_scale, rows * 4}, {k_scale, rows * 4}},
+                            {{q, 2 * e}, {k, 2 * e}}))
+            return fail(BSA_ERR_INVALID_ARGUMENT, "outputs must not overlap q, k or each other");
+    }
     if ((st = check_device()) != BSA_OK) return st;
     float* qbar = (float*)workspace;
     float* kbarT = qbar + (size_t)B * H * n * D;
@@ -271,6 +309,9 @@ bsa_status bsa_quantize_v_fp8(const void* v, int32_t B, int32_t H, int32_t S, in
     if (!v || !vt_e4m3 || !v_scale) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
     if (!aligned16(v) || !aligned16(vt_e4m3) || !aligned16(v_scale))
         return fail(BSA_ERR_INVALID_ARGUMENT, "v, vt_e4m3 and v_scale must be 16-byte aligned");
+    if (outputs_overlap({{vt_e4m3, bsa_vt_fp8_bytes(B, H, S, D, block)}, {v_scale, (size_t)B * H * D * 4}},
+                        {{v, elems(B, H, S, D) * 2}}))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "vt_e4m3 and v_scale must not overlap v or each other");
     if ((st = check_device()) != BSA_OK) return st;
     return hip_result(bsa::launch_quantize_v(v, B * H, S, D, block, vt_e4m3, v_scale, as_stream(hip_stream)),
                       "quantise V launch");
@@ -291,6 +332,9 @@ bsa_status bsa_quantize_fp8(const void* x, int32_t B, int32_t H, int32_t S, int3
     if (!x || !x_e4m3 || !scale) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
     if (!aligned16(x) || !aligned16(x_e4m3) || ((uintptr_t)scale & 3u))
         return fail(BSA_ERR_INVALID_ARGUMENT, "x and x_e4m3 must be 16-byte aligned");
+    if (outputs_overlap({{x_e4m3, elems(B, H, S, D)}, {scale, (size_t)B * H * bsa_num_blocks(S, block) * 4}},
+                        {{x, elems(B, H, S, D) * 2}}))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "x_e4m3 and scale must not overlap x or each other");
     if ((st = check_device()) != BSA_OK) return st;
     return hip_result(bsa::launch_quantize_fp8(x, B * H, S, D, block, x_e4m3, scale, as_stream(hip_stream)),
                       "quantize launch");

@@ -36,7 +36,9 @@
  *     workspace). The library never allocates device memory, never frees, and never
  *     synchronises; it keeps only a per-device table of properties.
  *   - Streams: every compute call is enqueued on hip_stream (a hipStream_t; NULL is the
- *     null stream) and returns before the GPU finishes. Outputs must not alias inputs.
+ *     null stream) and returns before the GPU finishes. No output's byte range may overlap
+ *     an input's or another output's (also checked: such a call returns
+ *     BSA_ERR_INVALID_ARGUMENT); inputs may overlap each other.
  *     A call only launches kernels (no memset, no copy, no synchronisation), so a sequence
  *     of calls can be captured into a HIP graph and replayed; selection with more than
  *     3968 blocks per sequence (D = 128; 4032 for D = 64) also raises the scoring kernel's

@@ -110,6 +110,104 @@ def test_fp8_calls_reject_bad_arguments():
     assert st == 2
 
 
+def P(a):
+    return ctypes.c_void_p(a)
+
+
+QA, KA, VA, RPA, CIA = 0x1000000, 0x2000000, 0x3000000, 0x4000000, 0x5000000
+TENSOR = 2 * 1024 * 64 * 2  # B=1, H=2, S=1024, D=64, bf16
+
+
+@pytest.mark.parametrize("out_at", [QA + 16, QA + TENSOR - 16, QA - TENSOR + 4096, VA + 4096, RPA - TENSOR + 64],
+                         ids=["q-start", "q-end", "ends-in-q", "in-v", "over-row_ptr"])
+def test_forward_rejects_any_overlap_of_out(out_at):
+    """out overlapping any part of q, v or row_ptr is refused, not only out == q."""
+    st = lib().bsa_forward(P(QA), P(KA), P(VA), 1, 2, 1024, 64, 64, P(RPA), P(CIA), P(out_at), None)
+    assert st == 1 and "overlap" in bsa.bsa_last_error(), bsa.bsa_last_error()
+
+
+def test_fp8_forwards_reject_out_over_their_operands():
+    # fp8 operands are 1 byte per element, the transposed full-fp8 V holds bsa_vt_fp8_bytes
+    st = lib().bsa_forward_fp8(P(QA), P(0x6000000), P(KA), P(0x7000000), P(VA), 1, 2, 1024, 64, 64, P(RPA), P(CIA),
+                               P(KA + TENSOR // 2 - 32), None)
+    assert st == 1 and "overlap" in bsa.bsa_last_error()
+    vt = bsa.bsa_vt_fp8_bytes(1, 2, 1024, 64, 64)
+    st = lib().bsa_forward_fp8_full(P(QA), P(0x6000000), P(KA), P(0x7000000), P(VA), P(0x8000000), 1, 2, 1024, 64, 64,
+                                    P(RPA), P(CIA), P(VA + vt - 32), None)
+    assert st == 1 and "overlap" in bsa.bsa_last_error()
+
+
+def test_select_and_quantisers_reject_overlapping_outputs():
+    big = 1 << 30
+    # col_idx (2*16*4 entries) running into the workspace
+    st = lib().bsa_select(P(0x10000), P(0x100000), 1, 2, 1024, 64, 64, 0.25, P(0x200000), P(0x300000),
+                          P(0x300000 + 64), big, None)
+    assert st == 1 and "overlap" in bsa.bsa_last_error()
+    # row_ptr inside k
+    st = lib().bsa_select(P(0x10000), P(0x100000), 1, 2, 1024, 64, 64, 0.25, P(0x100000 + 4096), P(0x300000),
+                          P(0x400000), big, None)
+    assert st == 1
+    # codes over the input
+    st = lib().bsa_quantize_fp8(P(0x10000), 1, 2, 1024, 64, 64, P(0x10000 + 1024), P(0x200000), None)
+    assert st == 1
+    st = lib().bsa_quantize_v_fp8(P(0x10000), 1, 2, 1024, 64, 64, P(0x200000), P(0x200000 + 4096), None)
+    assert st == 1
+    st = lib().bsa_pool(P(0x10000), 1, 2, 1024, 64, 64, P(0x10000 + 64 * 1024), None)
+    assert st == 1
+
+
+def test_binding_checks_caller_buffers_before_any_launch(monkeypatch):
+    """Undersized or misshapen outputs, CSR arrays of the wrong length and short workspaces
+    raise ValueError (TypeError for a wrong dtype) in the binding, before the library is asked
+    to launch anything. (The device check is relaxed to CPU tensors here; nothing reaches a
+    HIP call.)"""
+    import torch
+
+    real = bsa._dev_tensor
+
+    def cpu_ok(t, name, dtypes, ndim=4):
+        if isinstance(t, torch.Tensor) and t.device.type == "cpu":
+            if t.dtype not in dtypes:
+                raise TypeError(name)
+            if ndim is not None and t.dim() != ndim:
+                raise ValueError(name)
+            if not t.is_contiguous():
+                raise ValueError(name)
+            return t
+        return real(t, name, dtypes, ndim)
+
+    monkeypatch.setattr(bsa, "_dev_tensor", cpu_ok)
+    monkeypatch.setattr(bsa, "_stream", lambda t: (_ for _ in ()).throw(AssertionError("reached a launch")))
+    B, H, S, D, block = 1, 2, 300, 64, 64
+    n = bsa.bsa_num_blocks(S, block)
+    rows = B * H * n
+    q = torch.zeros(B, H, S, D, dtype=torch.bfloat16)
+    rp = torch.zeros(rows + 1, dtype=torch.int32)
+    ci = torch.zeros(rows * 2, dtype=torch.int32)
+    bad = [
+        lambda: bsa.bsa_forward(q, q, q, block, rp, ci, out=torch.empty(B, H, S - 1, D, dtype=torch.bfloat16)),
+        lambda: bsa.bsa_forward(q, q, q, block, rp[:-1], ci),
+        lambda: bsa.bsa_forward(q, q, q, block, rp, ci, out=torch.empty(B, H, S, D, dtype=torch.float32)),
+        lambda: bsa.bsa_pool(q, block, out=torch.empty(B, H, n - 1, D, dtype=torch.float32)),
+        lambda: bsa.bsa_select(q, q, block, 0.5, row_ptr=torch.empty(rows, dtype=torch.int32)),
+        lambda: bsa.bsa_select(q, q, block, 0.5, col_idx=torch.empty(rows * 2 - 1, dtype=torch.int32)),
+        lambda: bsa.bsa_select(q, q, block, 0.5, workspace=torch.empty(16, dtype=torch.uint8)),
+        lambda: bsa.bsa_quantize_fp8(q, block, codes=torch.empty(B, H, S, D - 1, dtype=torch.uint8)),
+        lambda: bsa.bsa_quantize_fp8(q, block, scale=torch.empty(rows - 1, dtype=torch.float32)),
+        lambda: bsa.bsa_quantize_v_fp8(q, block, scale=torch.empty(B * H * D - 1, dtype=torch.float32)),
+        lambda: bsa.bsa_select_quantize(q, q, block, 0.5, col_idx=torch.empty(1, dtype=torch.int32)),
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises((ValueError, TypeError)):
+            f()
+    x = torch.zeros(B, S, H, D, dtype=torch.bfloat16)
+    w = torch.zeros(H * D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bsa.bsa_norm_rope(x, w, block, (3, 10, 10), out=torch.empty(B, H, S, D - 8, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        bsa.bsa_norm_rope(x, w, block, (3, 10, 10), xbar=torch.empty(1, dtype=torch.float32))
+
+
 def gpu_visible():
     import torch
     return torch.cuda.is_available()
@@ -119,10 +217,12 @@ def test_no_device_status_without_gpu():
     if gpu_visible():
         pytest.skip("a GPU is visible; this checks the no-device path")
     a = [ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000)]
-    st = lib().bsa_forward(a[0], a[1], a[2], 1, 1, 128, 128, 128, FAKE, FAKE, ctypes.c_void_p(0x40000), None)
+    st = lib().bsa_forward(a[0], a[1], a[2], 1, 1, 128, 128, 128, ctypes.c_void_p(0x50000), FAKE,
+                           ctypes.c_void_p(0x40000), None)
     assert st == 4, bsa.bsa_last_error()
-    st = lib().bsa_select(a[0], a[1], 1, 1, 128, 128, 128, 0.5, FAKE, FAKE, FAKE, 1 << 20, None)
-    assert st == 4
+    st = lib().bsa_select(a[0], a[1], 1, 1, 128, 128, 128, 0.5, ctypes.c_void_p(0x50000), ctypes.c_void_p(0x60000),
+                          ctypes.c_void_p(0x70000), 1 << 20, None)
+    assert st == 4, bsa.bsa_last_error()
 
 
 def test_check_csr():

@@ -15,7 +15,8 @@ import torch
 import dynamic_block_sparse_bsa_amd as bsa
 import gen
 import oracle
-from parity import BF16_MAX, BF16_MEAN, FP8_MAX, check_fp8_full, check_lists, errors, to_dev, to_f64
+from parity import (BF16_MAX, BF16_MEAN, FP8_MAX, check_fp8_full, check_fp8_full_vs_unquantised, check_lists, errors,
+                    fp8_full_reference, to_dev, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +64,69 @@ def test_full_size_bf16(name):
     print("%s bf16 on oracle lists: max %.3e mean %.3e" % (name, mx, mean))
     assert mx <= BF16_MAX and mean <= BF16_MEAN
     del qd, kd, vd, out, out2
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,head", [("720p", 0), ("720p", -1), ("long", 0), ("long", -1)],
+                         ids=["720p-first-head", "720p-last-head", "long-first-head", "long-last-head"])
+def test_full_size_whole_head(name, head):
+    """Every output row of one whole head at full size: every query block (the partial last
+    one included) and so every workgroup position of the launch, for bf16 on the GPU's and
+    the oracle's lists and for fp8-QK against the unquantised attention."""
+    q, k, v, cfg, ref = workload(name)
+    B, H, S, D, block = q.shape + (cfg["block"],)
+    bh = head % (B * H)
+    n = oracle.num_blocks(S, block)
+    kept = ref["kept"]
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    rp, ci = bsa.bsa_select(qd, kd, block, cfg["keep_ratio"])
+    out = bsa.bsa_forward(qd, kd, vd, block, rp, ci)
+    orp, oci = torch.from_numpy(ref["row_ptr"]).cuda(), torch.from_numpy(ref["col_idx"]).cuda()
+    out_o = bsa.bsa_forward(qd, kd, vd, block, orp, oci)
+    q8, qs = bsa.bsa_quantize_fp8(qd, block)
+    k8, ks = bsa.bsa_quantize_fp8(kd, block)
+    out8 = bsa.bsa_forward_fp8(q8, qs, k8, ks, vd, block, rp, ci)
+    torch.cuda.synchronize()
+    grp, gci = rp.cpu().numpy(), ci.cpu().numpy()
+    tok = bh * S + np.arange(S)
+    expect = oracle.attention(q, k, v, block, grp, gci, tokens=tok)
+
+    got = to_f64(out[bh // H, bh % H])
+    mx, mean = errors(got, expect)
+    print("%s head %d bf16 on GPU lists, all %d rows: max %.3e mean %.3e" % (name, bh, S, mx, mean))
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+    # oracle lists: rows whose list differs from the GPU's are recomputed, the rest reuse expect
+    g_rows = gci.reshape(-1, kept)[bh * n:(bh + 1) * n]
+    o_rows = ref["col_idx"].reshape(-1, kept)[bh * n:(bh + 1) * n]
+    differ = np.nonzero(~(g_rows == o_rows).all(axis=1))[0]
+    expect_o = expect.copy()
+    if differ.size:
+        t_d = np.concatenate([np.arange(i * block, min(S, (i + 1) * block)) for i in differ])
+        expect_o[t_d] = oracle.attention(q, k, v, block, ref["row_ptr"], ref["col_idx"], tokens=bh * S + t_d)
+    mx, mean = errors(to_f64(out_o[bh // H, bh % H]), expect_o)
+    print("%s head %d bf16 on oracle lists (%d rows differ): max %.3e mean %.3e" % (name, bh, differ.size, mx, mean))
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+    got8 = to_f64(out8[bh // H, bh % H])
+    mx, mean = errors(got8, expect)
+    print("%s head %d fp8-QK vs unquantised: max %.3e mean %.3e" % (name, bh, mx, mean))
+    if name == "720p":  # the fp8 workload's shape: the stated fp8 bar against the true result
+        assert mx <= FP8_MAX
+    else:
+        # the long shape's stronger locality term makes attention peakier, and rounding Q and K
+        # to E4M3 alone moves some outputs past 6e-2 (measured 5.9e-2 on 3000 rows of one
+        # head); there the kernel is held to the bf16 bar against the oracle on the same E4M3
+        # operands, as on the small shapes
+        oq8, oqs = oracle.quantize_fp8(q, block)
+        ok8, oks = oracle.quantize_fp8(k, block)
+        assert np.array_equal(qs.cpu().numpy(), oqs) and np.array_equal(ks.cpu().numpy(), oks)
+        expect8 = oracle.attention_fp8(oq8, oqs, ok8, oks, v, block, grp, gci, tokens=tok)
+        mx8, mean8 = errors(got8, expect8)
+        print("%s head %d fp8-QK vs the oracle on the same E4M3 operands: max %.3e mean %.3e" % (name, bh, mx8, mean8))
+        assert mx8 <= BF16_MAX and mean8 <= BF16_MEAN
+    del qd, kd, vd, out, out_o, out8, q8, k8
     gc.collect()
     torch.cuda.empty_cache()
 
@@ -132,9 +196,12 @@ def test_full_size_fp8_full():
     grp, gci = rp.cpu().numpy(), ci.cpu().numpy()
     oq8, oqs = oracle.quantize_fp8(q, block)
     ok8, oks = oracle.quantize_fp8(k, block)
-    expect = oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, grp, gci, tokens=tok)
-    mx, mean, frac = check_fp8_full(got, expect)
-    print("fp8 full vs oracle: max %.3e mean %.3e rows beyond bf16 bar %.4f" % (mx, mean, frac))
+    expect, dev, nkeys = fp8_full_reference(oq8, oqs, ok8, oks, ov8, ovs, block, grp, gci, tokens=tok)
+    mx, mean, ratio = check_fp8_full(got, expect, dev, nkeys)
+    print("fp8 full vs exact attention on its E4M3 operands: max %.3e mean %.3e, %.2f of the bound" % (mx, mean, ratio))
     exact = oracle.attention(q, k, v, block, grp, gci, tokens=tok)
-    mx2, mean2 = errors(got, exact)
-    print("fp8 full vs unquantised attention (reported): max %.3e mean %.3e" % (mx2, mean2))
+    mx2, mean2 = check_fp8_full_vs_unquantised(got, expect, dev, nkeys, exact)
+    print("fp8 full vs unquantised attention: max %.3e mean %.3e" % (mx2, mean2))
+    assert mx2 <= FP8_MAX
+    sched = oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, grp, gci, tokens=tok)
+    print("diagnostic: fp8 full vs the 64-key sub-tile oracle: max %.3e mean %.3e" % errors(got, sched))

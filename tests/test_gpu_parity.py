@@ -14,7 +14,8 @@ import torch
 import dynamic_block_sparse_bsa_amd as bsa
 import gen
 import oracle
-from parity import BF16_MAX, BF16_MEAN, FP8_MAX, check_fp8_full, check_lists, errors, to_dev, to_f64
+from parity import (BF16_MAX, BF16_MEAN, FP8_MAX, check_fp8_full, check_fp8_full_vs_unquantised, check_lists, errors,
+                    fp8_full_reference, to_dev, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -128,6 +129,38 @@ def test_fp8(case):
     quant_only, _ = errors(expect8, expect)
     mx, _ = errors(out, expect)
     assert mx <= max(FP8_MAX, quant_only + BF16_MAX), (mx, quant_only)
+
+
+@pytest.mark.parametrize("D,block", [(128, 128), (64, 64)])
+def test_fp8_zero_and_underflowing_scales_with_a_ragged_tail(D, block):
+    """Zero block scales, and two tiny scales whose fp32 product underflows, next to the
+    partial last block: the masked keys of the tail must stay out of the softmax instead of
+    turning the row into NaN, and the logits of a zero-scale block are exactly zero."""
+    B, H, S = 1, 2, 3 * block - 37
+    q, k, v = gen.make_qkv(B, H, S, D, 37)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    n = oracle.num_blocks(S, block)
+    rows = B * H * n
+    rp = (np.arange(rows + 1) * n).astype(np.int32)
+    ci = np.tile(np.arange(n, dtype=np.int32), rows)
+    rpd, cid = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    _, _, q8, qs, k8, ks = bsa.bsa_select_quantize(qd, kd, block, 1.0)
+    qs[0, 0, 1] = 0.0
+    ks[0, 0, n - 1] = 0.0          # the partial block
+    qs[0, 1, :] = 1e-30
+    ks[0, 1, :] = 1e-30            # products underflow in fp32
+    qs_h, ks_h = qs.cpu().numpy(), ks.cpu().numpy()
+    q8_h, k8_h = q8.cpu().numpy(), k8.cpu().numpy()
+    out = to_f64(bsa.bsa_forward_fp8(q8, qs, k8, ks, vd, block, rpd, cid))
+    assert np.all(np.isfinite(out))
+    mx, mean = errors(out, oracle.attention_fp8(q8_h, qs_h, k8_h, ks_h, v, block, rp, ci))
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+    vt, vs = bsa.bsa_quantize_v_fp8(vd, block)
+    outf = to_f64(bsa.bsa_forward_fp8_full(q8, qs, k8, ks, vt, vs, block, rpd, cid))
+    assert np.all(np.isfinite(outf))
+    ov8, ovs = oracle.quantize_v_fp8(v)
+    expect, dev, nkeys = fp8_full_reference(q8_h, qs_h, k8_h, ks_h, ov8, ovs, block, rp, ci)
+    check_fp8_full(outf, expect, dev, nkeys)
 
 
 def test_streams_are_honoured():
@@ -288,8 +321,10 @@ def test_fp8_full_forward(case):
     oq8, oqs = oracle.quantize_fp8(q, block)
     ok8, oks = oracle.quantize_fp8(k, block)
     ov8, ovs = oracle.quantize_v_fp8(v)
-    expect = oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, ref["row_ptr"], ref["col_idx"])
-    check_fp8_full(out, expect)
+    expect, dev, nkeys = fp8_full_reference(oq8, oqs, ok8, oks, ov8, ovs, block, ref["row_ptr"], ref["col_idx"])
+    check_fp8_full(out, expect, dev, nkeys)
+    exact = oracle.attention(q, k, v, block, ref["row_ptr"], ref["col_idx"])
+    check_fp8_full_vs_unquantised(out, expect, dev, nkeys, exact)
 
 
 def test_fp8_full_forward_rising_scores_and_ragged_lists():
@@ -316,8 +351,9 @@ def test_fp8_full_forward_rising_scores_and_ragged_lists():
     oq8, oqs = oracle.quantize_fp8(q, block)
     ok8, oks = oracle.quantize_fp8(k, block)
     ov8, ovs = oracle.quantize_v_fp8(v)
-    expect = oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, rp, ci)
-    check_fp8_full(out, expect)
+    expect, dev, nkeys = fp8_full_reference(oq8, oqs, ok8, oks, ov8, ovs, block, rp, ci)
+    check_fp8_full(out, expect, dev, nkeys)
+    check_fp8_full_vs_unquantised(out, expect, dev, nkeys, oracle.attention(q, k, v, block, rp, ci))
     assert np.all(out[0, 0, block:2 * block] == 0.0)  # row 1 has an empty list
 
 
@@ -368,7 +404,8 @@ def test_random_shapes_all_paths(i):
     ov8, ovs = oracle.quantize_v_fp8(v)
     assert np.array_equal(vts.cpu().numpy(), ovs)
     outf = to_f64(bsa.bsa_forward_fp8_full(qf8, qfs, kf8, kfs, vt8, vts, block, rp, ci))
-    check_fp8_full(outf, oracle.attention_fp8_full(oq8, oqs, ok8, oks, ov8, ovs, block, grp, gci))
+    expect, dev, nkeys = fp8_full_reference(oq8, oqs, ok8, oks, ov8, ovs, block, grp, gci)
+    check_fp8_full(outf, expect, dev, nkeys)
 
 
 @pytest.mark.parametrize("S,block,r", [(1100 * 64 - 13, 64, 0.1), (1030 * 64, 64, 0.02), (1025 * 128 - 1, 128, 0.05)])

@@ -641,3 +641,28 @@ def test_fp8_full_sub_tile_is_64_keys():
     w_rounded = np.concatenate([e4m3_round(448 * np.exp2((xa - xb) * math.log2(math.e)))[None].repeat(64) / 448, np.ones(64)])
     assert np.max(np.abs((w_rounded @ vhat) / w_rounded.sum() - expect)) > 1e-6  # the two readings differ here
     assert np.max(np.abs(out[0] - expect)) <= 1e-12
+
+
+@pytest.mark.parametrize("seed,rising,S,D,block,r", [(47, False, 1000, 128, 128, 0.3), (48, True, 6 * 128 - 40, 128, 128, 0.6),
+                                                   (49, True, 777, 64, 64, 0.5), (50, False, 1090, 64, 128, 0.5)])
+def test_fp8_full_schedule_oracle_within_the_schedule_free_bound(seed, rising, S, D, block, r):
+    # The 64-key sub-tile oracle (one order of work and one sequence of reference points) is
+    # one instance of the full fp8 path: it must meet the schedule-free criterion that the
+    # GPU kernel is held to, element bound and mean bar, including rows whose maximum moves.
+    from parity import check_fp8_full, keys_per_token
+    B, H = 1, 2
+    q, k, v = gen.make_qkv(B, H, S, D, seed, grid=(S // 10, 10, 1) if S % 10 == 0 else None, alpha=0.5)
+    if rising:
+        kf = f32(k)
+        for j in range(oracle.num_blocks(S, block)):
+            kf[:, :, j * block:(j + 1) * block] *= 1.0 + 0.7 * j
+        k = bf16(kf)
+    q8, qs = oracle.quantize_fp8(q, block)
+    k8, ks = oracle.quantize_fp8(k, block)
+    v8, vs = oracle.quantize_v_fp8(v)
+    sel = oracle.select(q, k, block, r)
+    rp, ci = sel["row_ptr"], sel["col_idx"]
+    sched = oracle.attention_fp8_full(q8, qs, k8, ks, v8, vs, block, rp, ci)
+    exact, dev = oracle.attention_fp8_qkv(q8, qs, k8, ks, v8, vs, block, rp, ci, spread=True)
+    mx, mean, ratio = check_fp8_full(sched, exact, dev, keys_per_token(rp, ci, B, H, S, block))
+    assert 0.0 < mx and ratio < 1.0
