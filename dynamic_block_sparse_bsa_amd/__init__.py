@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "BsaError", "lib_path", "bsa_num_blocks", "bsa_num_kept", "bsa_select_workspace_bytes",
-    "bsa_pool", "bsa_select", "bsa_forward", "bsa_quantize_fp8", "bsa_forward_fp8",
+    "bsa_pool", "bsa_select", "bsa_select_noalloc", "bsa_select_noalloc_max_bytes", "bsa_forward", "bsa_quantize_fp8", "bsa_forward_fp8",
     "bsa_check_csr", "bsa_status_string", "bsa_last_error", "bsa_vt_fp8_bytes", "bsa_select_quantize",
     "bsa_quantize_v_fp8", "bsa_forward_fp8_full", "bsa_norm_rope_workspace_bytes", "bsa_norm_rope",
     "bsa_norm_rope_select_workspace_bytes", "bsa_norm_rope_select",
@@ -52,6 +52,8 @@ def _load():
         "bsa_select_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "bsa_pool": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P]),
         "bsa_select": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, f64, P, P, P, sz, P]),
+        "bsa_select_noalloc": (ctypes.c_int, [P, P, i32, i32, i32, i32, i32, f64, P, P, P]),
+        "bsa_select_noalloc_max_bytes": (sz, []),
         "bsa_forward": (ctypes.c_int, [P, P, P, i32, i32, i32, i32, i32, P, P, P, P]),
         "bsa_quantize_fp8": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P]),
         "bsa_forward_fp8": (ctypes.c_int, [P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]),
@@ -179,6 +181,34 @@ def bsa_select(q, k, block: int, keep_ratio: float, workspace=None, row_ptr=None
     _given(col_idx, "col_idx", (torch.int32,), rows * kept, q.device)
     _check(_load().bsa_select(_p(q), _p(k), B, H, S, D, block, keep_ratio, _p(row_ptr), _p(col_idx),
                               _p(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
+    return row_ptr, col_idx
+
+
+def bsa_select_noalloc_max_bytes() -> int:
+    return _load().bsa_select_noalloc_max_bytes()
+
+
+def bsa_select_noalloc(q, k, block: int, keep_ratio: float, row_ptr=None, col_idx=None):
+    """bsa_select with the block means in the library's own scratch array: the C call
+    allocates nothing (pass row_ptr and col_idx to keep this function allocation-free too)."""
+    _dev_tensor(q, "q", (torch.bfloat16,))
+    _dev_tensor(k, "k", (torch.bfloat16,))
+    if q.shape != k.shape:
+        raise ValueError("q and k shapes differ")
+    B, H, S, D = q.shape
+    n = bsa_num_blocks(S, block)
+    kept = bsa_num_kept(n, keep_ratio)
+    if kept == 0:
+        raise BsaError(1, "keep_ratio must be in (0, 1] (got %r)" % (keep_ratio,))
+    rows = B * H * n
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
+    if col_idx is None:
+        col_idx = torch.empty(rows * kept, dtype=torch.int32, device=q.device)
+    _given(row_ptr, "row_ptr", (torch.int32,), rows + 1, q.device)
+    _given(col_idx, "col_idx", (torch.int32,), rows * kept, q.device)
+    _check(_load().bsa_select_noalloc(_p(q), _p(k), B, H, S, D, block, keep_ratio, _p(row_ptr), _p(col_idx),
+                                      _stream(q)))
     return row_ptr, col_idx
 
 

@@ -148,6 +148,37 @@ bsa::NormRopeArgs norm_rope_args(const void* x, const void* w, void* out, float*
     return a;
 }
 
+// Scratch memory of bsa_select_noalloc: the pooled means that bsa_select keeps in the
+// caller's workspace live here instead. One copy per device, at its own address, held until
+// the process ends; host code uses only the address hipGetSymbolAddress returns for it.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch;  // per device: the device address of `scratch`, once looked up
+
+// The device address of `scratch` on the current device (looked up on first use).
+bsa_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(BSA_ERR_NO_DEVICE, "no HIP device is available");
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1, nullptr);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(BSA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+        }
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return BSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -205,6 +236,37 @@ bsa_status bsa_select(const void* q, const void* k, int32_t B, int32_t H, int32_
         return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr, col_idx and workspace must not overlap q, k or each other");
     if ((st = check_device()) != BSA_OK) return st;
     float* qbar = (float*)workspace;
+    float* kbarT = qbar + (size_t)B * H * n * D;
+    hipStream_t s = as_stream(hip_stream);
+    if ((st = hip_result(bsa::launch_pool_qk(q, k, B * H, S, D, block, qbar, kbarT, s), "pool launch")) != BSA_OK) return st;
+    return hip_result(bsa::launch_select(qbar, kbarT, B * H, n, D, kept, row_ptr, col_idx, s), "select launch");
+}
+
+size_t bsa_select_noalloc_max_bytes(void) { return kScratchBytes; }
+
+bsa_status bsa_select_noalloc(const void* q, const void* k, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
+                              double keep_ratio, int32_t* row_ptr, int32_t* col_idx, void* hip_stream) {
+    bsa_status st = check_shape(B, H, S, D, block);
+    if (st != BSA_OK) return st;
+    if (!q || !k || !row_ptr || !col_idx) return fail(BSA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(q) || !aligned16(k)) return fail(BSA_ERR_INVALID_ARGUMENT, "q and k must be 16-byte aligned");
+    if (((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u)) return fail(BSA_ERR_INVALID_ARGUMENT, "misaligned CSR arrays");
+    const int32_t n = bsa_num_blocks(S, block);
+    const int32_t kept = bsa_num_kept(n, keep_ratio);
+    if (kept == 0) return fail(BSA_ERR_INVALID_ARGUMENT, "keep_ratio must be in (0, 1] (got %g)", keep_ratio);
+    if (n > bsa::kMaxSelectBlocks) return fail(BSA_ERR_UNSUPPORTED, "bsa_select_noalloc supports at most %d blocks per sequence (got %d)", bsa::kMaxSelectBlocks, n);
+    if ((int64_t)B * H * n * kept >= ((int64_t)1 << 31)) return fail(BSA_ERR_UNSUPPORTED, "kept-block list too long for int32 indices");
+    const size_t need = bsa_select_workspace_bytes(B, H, S, D, block);
+    if (need > kScratchBytes)
+        return fail(BSA_ERR_UNSUPPORTED, "bsa_select_noalloc holds at most %zu bytes of block means; this shape needs %zu (use bsa_select with a workspace)",
+                    kScratchBytes, need);
+    const size_t rows = (size_t)B * H * n, tbytes = elems(B, H, S, D) * 2;
+    if (outputs_overlap({{row_ptr, (rows + 1) * 4}, {col_idx, rows * kept * 4}}, {{q, tbytes}, {k, tbytes}}))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr and col_idx must not overlap q, k or each other");
+    if ((st = check_device()) != BSA_OK) return st;
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws)) != BSA_OK) return st;
+    float* qbar = (float*)ws;
     float* kbarT = qbar + (size_t)B * H * n * D;
     hipStream_t s = as_stream(hip_stream);
     if ((st = hip_result(bsa::launch_pool_qk(q, k, B * H, S, D, block, qbar, kbarT, s), "pool launch")) != BSA_OK) return st;

@@ -106,6 +106,21 @@ bsa_status bsa_select(const void* q, const void* k, int32_t B, int32_t H, int32_
                       int32_t block, double keep_ratio, int32_t* row_ptr, int32_t* col_idx,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* bsa_select without a workspace argument, for callers that cannot allocate device memory
+ * at call time: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, results and errors as bsa_select, except that the block means
+ * go to a scratch array inside the library: one per device, bsa_select_noalloc_max_bytes()
+ * = 64 MiB, held by each device the library runs on until the process ends (found once per
+ * device on its first call). The call allocates nothing. Shapes whose means need more than
+ * that (bsa_select_workspace_bytes() > bsa_select_noalloc_max_bytes(), i.e. B*H*n*D >
+ * 8 Mi) return BSA_ERR_UNSUPPORTED. Every call on a device shares its scratch array, so
+ * calls on one device whose executions overlap (different streams, several threads) race;
+ * nothing in the array needs to start at zero. */
+size_t bsa_select_noalloc_max_bytes(void);
+bsa_status bsa_select_noalloc(const void* q, const void* k, int32_t B, int32_t H, int32_t S,
+                              int32_t D, int32_t block, double keep_ratio, int32_t* row_ptr,
+                              int32_t* col_idx, void* hip_stream);
+
 /* Sparse attention over the kept blocks ([KC] 动态稀疏量化注意力: only the activated key
  * blocks are computed; [AO] 动态稀疏注意力: dense inside each selected block). For query
  * token t of block i: out_t = sum_u softmax_u(q_t . k_u / sqrt(D)) v_u over the valid

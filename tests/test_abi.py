@@ -208,6 +208,16 @@ def test_binding_checks_caller_buffers_before_any_launch(monkeypatch):
         bsa.bsa_norm_rope(x, w, block, (3, 10, 10), xbar=torch.empty(1, dtype=torch.float32))
 
 
+def test_noalloc_select_rejects_shapes_beyond_its_scratch():
+    # 2*B*H*n*D*4 bytes of means: 80 heads of 960 blocks at D=128 need 78.6 MB > 64 MiB
+    assert bsa.bsa_select_noalloc_max_bytes() == 64 << 20
+    st = lib().bsa_select_noalloc(P(0x1000000), P(0x40000000), 1, 80, 122880, 128, 128, 0.1, P(0x80000000),
+                                  P(0x90000000), None)
+    assert st == 2 and "at most" in bsa.bsa_last_error(), bsa.bsa_last_error()
+    st = lib().bsa_select_noalloc(None, P(0x40000000), 1, 2, 1024, 64, 64, 0.25, P(0x80000000), P(0x90000000), None)
+    assert st == 1
+
+
 def gpu_visible():
     import torch
     return torch.cuda.is_available()
