@@ -346,12 +346,183 @@ def power(args):
                           "idle_gfx_clock_mhz": round(sum(c for _, c in idle) / len(idle), 1)}), flush=True)
 
 
+PEAK_LIB = os.path.join(ROOT, "dynamic_block_sparse_bsa_amd", "libbsa_peak.so")
+
+
+def mfma_peak(dev, seconds=0.25):
+    """Measured dense MFMA throughput (TFLOP/s) of this card, bf16 and fp8: every SIMD issues
+    independent MFMAs with register operands (dynamic_block_sparse_bsa_amd/csrc/peak.hip).
+    The attention kernels' rates are also given as fractions of these ceilings."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(PEAK_LIB)
+    lib.bsa_peak_run.restype = ctypes.c_int
+    lib.bsa_peak_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsa_peak_flops.restype = ctypes.c_double
+    lib.bsa_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    wgs = 256 * 8
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, fp8 in (("bf16", 0), ("fp8", 1)):
+        iters = 64
+        while True:  # grow the launch until it runs for about `seconds`
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if lib.bsa_peak_run(fp8, wgs, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream)):
+                raise RuntimeError("peak probe launch failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            if ms >= seconds * 1e3 or iters >= 1 << 20:
+                break
+            iters *= 2
+        out[name + "_tflops"] = round(lib.bsa_peak_flops(fp8, wgs, iters) / (ms * 1e-3) / 1e12, 1)
+    return out
+
+
+def time_calls(fns, steps, warmup):
+    """Times each callable of fns (run in turn, as one step) with HIP events on torch's current
+    stream, the stream every call is enqueued on; returns per-callable lists of ms."""
+    import torch
+
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, f in enumerate(fns):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    return [[ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)] for j in range(len(fns))]
+
+
+def stats(ms):
+    return {"mean": round(float(np.mean(ms)), 4), "median": round(float(np.median(ms)), 4),
+            "min": round(float(np.min(ms)), 4)}
+
+
+def head_slice(q, k, v, heads):
+    """The first `heads` heads of each tensor: one rank's share when heads are sharded."""
+    if not heads:
+        return q, k, v
+    return tuple(np.ascontiguousarray(x[:, :heads]) for x in (q, k, v))
+
+
+def all_configs(args):
+    """One JSON line per configuration: tiny, 480p, 720p, 720p dense (keep_ratio 1), long and
+    fp8-QK on the 720p tensors. Each line carries the GPU select and forward times (mean,
+    median, min), the kept-block TFLOP/s and its fractions of the published and the measured
+    MFMA peak, the selection's HBM rate, and the oracle on this host's cores: its whole
+    selection, and its attention on a stated sample of query rows scaled to the whole call
+    (all rows for tiny; not run for the dense line)."""
+    import torch
+
+    import dynamic_block_sparse_bsa_amd as bsa
+    import gen
+    import oracle
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    peak = mfma_peak(dev)
+    print(json.dumps({"mfma_peak_measured": peak}), flush=True)
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    for name in ("tiny", "480p", "720p", "long"):
+        q, k, v, cfg = gen.make_config(name)
+        q, k, v = head_slice(q, k, v, args.heads)
+        B, H, S, D = q.shape
+        block, r = cfg["block"], cfg["keep_ratio"]
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        n = bsa.bsa_num_blocks(S, block)
+        rows = B * H * n
+        runs = [(r, False)] + ([(1.0, True)] if name == "720p" else []) + ([(r, "fp8")] if name == "720p" else [])
+        for ratio, kind in runs:
+            kept = bsa.bsa_num_kept(n, ratio)
+            out = torch.empty_like(qd)
+            if kind is True:  # dense: every key block, no selection
+                rp = torch.arange(rows + 1, dtype=torch.int32, device=dev) * n
+                ci = torch.arange(n, dtype=torch.int32, device=dev).repeat(rows)
+                fwd, = time_calls([lambda: bsa.bsa_forward(qd, kd, vd, block, rp, ci, out=out)], 3, 1)
+                sel = None
+            else:
+                ws = torch.empty(bsa.bsa_select_workspace_bytes(B, H, S, D, block), dtype=torch.uint8, device=dev)
+                rp = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+                ci = torch.empty(rows * kept, dtype=torch.int32, device=dev)
+                select = lambda: bsa.bsa_select(qd, kd, block, ratio, workspace=ws, row_ptr=rp, col_idx=ci)
+                if kind == "fp8":
+                    q8, qs = bsa.bsa_quantize_fp8(qd, block)
+                    k8, ks = bsa.bsa_quantize_fp8(kd, block)
+                    quant = lambda: (bsa.bsa_quantize_fp8(qd, block, codes=q8, scale=qs),
+                                     bsa.bsa_quantize_fp8(kd, block, codes=k8, scale=ks))
+                    sel, qt, fwd = time_calls([select, quant, lambda: bsa.bsa_forward_fp8(q8, qs, k8, ks, vd, block, rp, ci,
+                                                                                           out=out)],
+                                              args.steps, args.warmup)
+                else:
+                    sel, fwd = time_calls([select, lambda: bsa.bsa_forward(qd, kd, vd, block, rp, ci, out=out)],
+                                          args.steps, args.warmup)
+            flop = 4.0 * D * kept_flops(rp.cpu().numpy(), ci.cpu().numpy(), S, block)
+            tf = flop / (np.mean(fwd) * 1e-3) / 1e12
+            label = name + (" dense" if kind is True else " fp8-QK" if kind == "fp8" else "")
+            line = {"workload": "%s: B=%d H=%d S=%d D=%d block=%d keep_ratio=%g (%d of %d key blocks kept)"
+                                % (label, B, H, S, D, block, ratio, kept, n),
+                    "attention_ms": stats(fwd), "kept_tflop_per_call": round(flop / 1e12, 4),
+                    "kept_tflops": round(tf, 1), "frac_bf16_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                    "frac_measured_bf16_peak": round(tf / peak["bf16_tflops"], 4)}
+            if kind == "fp8":
+                mixed = 2 / (1 / FP8_PEAK_TFLOPS + 1 / BF16_PEAK_TFLOPS)
+                line["quantize_ms"] = stats(qt)
+                line["frac_mixed_fp8_bf16_peak"] = round(tf / mixed, 4)
+            if sel is not None:
+                line["select_ms"] = stats(sel)
+                line["select_hbm_gbs"] = round(2 * B * H * S * D * 2 / (np.mean(sel) * 1e-3) / 1e9, 1)
+            if not args.no_cpu_baseline and kind is not True:
+                t0 = time.perf_counter()
+                ref = oracle.select(q, k, block, ratio)
+                t_sel = time.perf_counter() - t0
+                sample = B * H * S if name == "tiny" else min(B * H * S, args.cpu_sample)
+                tok = np.sort(np.random.default_rng(0).choice(B * H * S, size=sample, replace=False))
+                t0 = time.perf_counter()
+                if kind == "fp8":
+                    oq8, oqs = oracle.quantize_fp8(q, block)
+                    ok8, oks = oracle.quantize_fp8(k, block)
+                    oracle.attention_fp8(oq8, oqs, ok8, oks, v, block, ref["row_ptr"], ref["col_idx"], tokens=tok)
+                else:
+                    oracle.attention(q, k, v, block, ref["row_ptr"], ref["col_idx"], tokens=tok)
+                t_att = (time.perf_counter() - t0) * (B * H * S) / sample
+                line["cpu_baseline"] = {"kind": "oracle", "cores": int(os.environ["OMP_NUM_THREADS"]),
+                                        "select_s": round(t_sel, 3), "attention_s": round(t_att, 2),
+                                        "sample": "whole selection; attention on %d of %d query rows%s"
+                                                  % (sample, B * H * S, "" if sample == B * H * S else ", scaled")}
+            print(json.dumps(line), flush=True)
+            del rp, ci, out
+        del qd, kd, vd, q, k, v
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="720p", choices=["480p", "720p", "long"])
+    ap.add_argument("--heads", type=int, default=0,
+                    help="run only the first HEADS heads of the workload: one rank's share when the "
+                         "heads are sharded across GPUs (5 of 40 on eight GPUs)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead: one JSON line per configuration (tiny, 480p, 720p, 720p dense, long, "
+                         "fp8-QK) with the oracle timed beside each")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="instead: print the card's measured dense bf16 and fp8 MFMA throughput")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8192, help="query rows the CPU oracle computes")
     ap.add_argument("--no-dense", action="store_true")
@@ -381,6 +552,14 @@ def main():
     if args.norm_rope:
         norm_rope(args)
         return
+    if args.all_configs:
+        all_configs(args)
+        return
+    if args.mfma_peak:
+        import torch
+
+        print(json.dumps({"mfma_peak_measured": mfma_peak(torch.device("cuda:0"), seconds=1.0)}), flush=True)
+        return
 
     import torch
 
@@ -392,6 +571,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     q, k, v, cfg = gen.make_config(args.config)
+    q, k, v = head_slice(q, k, v, args.heads)
     B, H, S, D = q.shape
     block, r = cfg["block"], cfg["keep_ratio"]
     to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -399,6 +579,7 @@ def main():
     n = bsa.bsa_num_blocks(S, block)
     kept = bsa.bsa_num_kept(n, r)
     rows = B * H * n
+    peak = mfma_peak(dev)
     ws = torch.empty(bsa.bsa_select_workspace_bytes(B, H, S, D, block), dtype=torch.uint8, device=dev)
     rp = torch.empty(rows + 1, dtype=torch.int32, device=dev)
     ci = torch.empty(rows * kept, dtype=torch.int32, device=dev)
@@ -521,8 +702,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded noise + smooth (t,h,w) locality term, bf16)",
-        "config": {"workload": "%s: B=%d H=%d S=%d D=%d block=%d keep_ratio=%g (%d of %d key blocks kept)"
-                               % (args.config, B, H, S, D, block, r, kept, n),
+        "config": {"workload": "%s%s: B=%d H=%d S=%d D=%d block=%d keep_ratio=%g (%d of %d key blocks kept)"
+                               % (args.config, " (first %d heads: one rank's share)" % H if args.heads else "",
+                                  B, H, S, D, block, r, kept, n),
                    "global_batch": B, "seq_len": S, "heads": H, "head_dim": D, "block": block,
                    "keep_ratio": r, "parallelism": "single GPU"},
         "attention_ms": round(fwd_ms, 4),
@@ -539,8 +721,11 @@ def main():
         "select_hbm_gbs": round(pool_bytes / (sel_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profile(kernel_sha),
-                     "kernel": "attn_kernel<128,128,bf16>"},
+                     "traffic": traffic_from_profile(kernel_sha) if not args.heads else None,
+                     "kernel": "attn_kernel<128,128,bf16>",
+                     "measured_peak": peak["bf16_tflops"],
+                     "frac_measured_peak": round(fwd_tflops / peak["bf16_tflops"], 4)},
+        "mfma_peak_measured": peak,
         "fp8_qk": {"quantize_ms": round(quant_ms, 4), "attention_ms": round(fwd8_ms, 4),
                    "kept_tflops": round(flop / (fwd8_ms * 1e-3) / 1e12, 1),
                    "frac_mixed_peak": round(flop / (fwd8_ms * 1e-3) / 1e12 / (2 / (1 / FP8_PEAK_TFLOPS + 1 / BF16_PEAK_TFLOPS)), 4),
@@ -549,6 +734,7 @@ def main():
                      "attention_ms": round(fwdf_ms, 4),
                      "kept_tflops": round(flop / (fwdf_ms * 1e-3) / 1e12, 1),
                      "frac_fp8_mfma_peak": round(flop / (fwdf_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                     "frac_measured_fp8_peak": round(flop / (fwdf_ms * 1e-3) / 1e12 / peak["fp8_tflops"], 4),
                      "step_ms": round(selq_ms + vq_ms + fwdf_ms, 4)},
         "dense_keep_ratio_1": dense,
         "cpu_baseline": cpu,

@@ -7,6 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsa.so")
 SOURCES = ["attention.hip", "select.hip", "fp8.hip", "normrope.hip", "bsa_api.hip"]
+PEAK_SOURCE = "peak.hip"
+PEAK_LIB = os.path.join(HERE, "libbsa_peak.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-strict-aliasing",
@@ -34,11 +36,14 @@ def build(verbose: bool = False) -> str:
             print(msg, flush=True)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(compile_one, SOURCES + [PEAK_SOURCE]))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs[:-1]
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    # the benchmark's MFMA throughput probe: a library of its own, outside libbsa's ABI
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", PEAK_LIB + ".tmp", objs[-1]], check=True)
+    os.replace(PEAK_LIB + ".tmp", PEAK_LIB)
     return LIB
 
 
