@@ -227,6 +227,8 @@ static void attention_core(const tensor_t* Q, const tensor_t* K, const tensor_t*
                 for (int64_t u = u0; u < u1; ++u) key[nk++] = u;
             }
             for (int64_t d = 0; d < D; ++d) { qrow[d] = load(Q, bh, t, d); o[d] = 0.0; }
+            if (dev)  /* an empty row has no spread */
+                for (int64_t d = 0; d < 3 * D; ++d) dev[m * 3 * D + d] = 0.0;
             if (nk == 0) continue;
             double mx = -INFINITY;
             for (int64_t a = 0; a < nk; ++a) {
@@ -243,7 +245,6 @@ static void attention_core(const tensor_t* Q, const tensor_t* K, const tensor_t*
             }
             if (dev) {
                 double* dv = dev + m * 3 * D;
-                for (int64_t d = 0; d < 3 * D; ++d) dv[d] = 0.0;
                 for (int64_t a = 0; a < nk; ++a) {
                     double p = logit[a] / denom;
                     for (int64_t d = 0; d < D; ++d) {

@@ -666,3 +666,21 @@ def test_fp8_full_schedule_oracle_within_the_schedule_free_bound(seed, rising, S
     exact, dev = oracle.attention_fp8_qkv(q8, qs, k8, ks, v8, vs, block, rp, ci, spread=True)
     mx, mean, ratio = check_fp8_full(sched, exact, dev, keys_per_token(rp, ci, B, H, S, block))
     assert 0.0 < mx and ratio < 1.0
+
+
+def test_fp8_qkv_empty_rows_have_zero_output_and_zero_spread():
+    # A row with an empty list attends to nothing (reading R13): zero output, and no spread for
+    # the full fp8 bound to add, even when the result buffers start out as garbage.
+    B, H, S, D, block = 1, 2, 256, 16, 64
+    q, k, v = gen.make_qkv(B, H, S, D, 95)
+    q8, qs = oracle.quantize_fp8(q, block)
+    k8, ks = oracle.quantize_fp8(k, block)
+    v8, vs = oracle.quantize_v_fp8(v)
+    rp = np.array([0, 0, 2, 2, 4, 4, 4, 5, 5], np.int32)
+    ci = np.array([0, 1, 2, 3, 1], np.int32)
+    for _ in range(3):
+        out, dev = oracle.attention_fp8_qkv(q8, qs, k8, ks, v8, vs, block, rp, ci, spread=True)
+        for bh, i in [(0, 0), (0, 2), (1, 1), (1, 3)]:
+            rows = slice(i * block, (i + 1) * block)
+            assert np.all(out[0, bh, rows] == 0.0) and np.all(dev[0, bh, rows] == 0.0)
+        assert np.all(dev[0, 0, block:2 * block, 1] > 0.0)
