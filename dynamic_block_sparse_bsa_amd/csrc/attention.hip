@@ -405,16 +405,17 @@ attn_kernel(const AttnArgs a) {
         // sub-tile, where m_used is still -inf, or when scores climb far above m_used -- is
         // the sub-tile's maximum computed and the reference point raised (the accumulators
         // rescaled by the same factor). The result does not depend on the reference point.
+        // The row sum takes the fp32 weights with plain adds: a bf16 dot2 would do it in half
+        // the instructions, but dot instructions wait behind the other wave's MFMAs on the
+        // SIMD, and plain adds do not.
         auto form = [&](int km, bf16x8& pk, float& l) {
+            float pw[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pk[e] = (__bf16)fast_exp2(__builtin_fmaf(s[km >> 1][8 * (km & 1) + e], tscale, -m_used));
-            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bf16x2 pr = {pk[2 * e], pk[2 * e + 1]};
-                l = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l, false);
+            for (int e = 0; e < 8; ++e) {
+                pw[e] = fast_exp2(__builtin_fmaf(s[km >> 1][8 * (km & 1) + e], tscale, -m_used));
+                pk[e] = (__bf16)pw[e];
             }
+            l += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
         };
         auto raise_reference = [&]() {
             float mx = s[0][0];
