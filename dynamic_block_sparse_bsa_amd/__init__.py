@@ -57,7 +57,7 @@ def _load():
         "bsa_forward": (ctypes.c_int, [P, P, P, i32, i32, i32, i32, i32, P, P, P, P]),
         "bsa_quantize_fp8": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P]),
         "bsa_forward_fp8": (ctypes.c_int, [P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]),
-        "bsa_check_csr": (ctypes.c_int, [P, P, i32, i32]),
+        "bsa_check_csr": (ctypes.c_int, [P, ctypes.c_int64, P, ctypes.c_int64, i32, i32]),
         "bsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "bsa_last_error": (ctypes.c_char_p, []),
         "bsa_vt_fp8_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -361,13 +361,10 @@ def bsa_forward_fp8_full(q8, q_scale, k8, k_scale, vt8, v_scale, block: int, row
 def bsa_check_csr(row_ptr, col_idx, rows: int, n_blocks: int):
     """Validate a host-side CSR (numpy or CPU tensors); raises BsaError on a violation."""
     import numpy as np
-    rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
-    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
-    if rp.size != rows + 1:
-        raise BsaError(1, "row_ptr must have rows + 1 entries")
-    if rp[-1] > ci.size:
-        raise BsaError(1, "col_idx shorter than row_ptr[rows]")
-    _check(_load().bsa_check_csr(ctypes.c_void_p(rp.ctypes.data), ctypes.c_void_p(ci.ctypes.data), rows, n_blocks))
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int32).reshape(-1)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32).reshape(-1)
+    _check(_load().bsa_check_csr(ctypes.c_void_p(rp.ctypes.data), rp.size, ctypes.c_void_p(ci.ctypes.data), ci.size,
+                                 rows, n_blocks))
 
 
 def bsa_status_string(status: int) -> str:

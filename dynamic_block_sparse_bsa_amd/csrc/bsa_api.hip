@@ -474,12 +474,19 @@ bsa_status bsa_norm_rope_select(const void* xq, const void* xk, const void* wq, 
     return hip_result(bsa::launch_select(qbar, kbarT, B * H, n, D, kept, row_ptr, col_idx, s), "select launch");
 }
 
-bsa_status bsa_check_csr(const int32_t* row_ptr, const int32_t* col_idx, int32_t rows, int32_t n_blocks) {
-    if (!row_ptr || rows < 0 || n_blocks < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "bad arguments");
+bsa_status bsa_check_csr(const int32_t* row_ptr, int64_t row_ptr_len, const int32_t* col_idx, int64_t col_idx_len,
+                         int32_t rows, int32_t n_blocks) {
+    if (!row_ptr || rows < 0 || n_blocks < 1 || col_idx_len < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "bad arguments");
+    if (row_ptr_len != (int64_t)rows + 1)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr has %lld entries, expected rows + 1 = %lld", (long long)row_ptr_len,
+                    (long long)rows + 1);
     if (row_ptr[0] != 0) return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr[0] = %d, expected 0", row_ptr[0]);
     for (int32_t r = 0; r < rows; ++r) {
         const int32_t a = row_ptr[r], b = row_ptr[r + 1];
         if (b < a) return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr decreases at row %d", r);
+        if ((int64_t)b > col_idx_len)
+            return fail(BSA_ERR_INVALID_ARGUMENT, "row %d ends at %d, past col_idx's %lld entries", r, b,
+                        (long long)col_idx_len);
         if (b > a && !col_idx) return fail(BSA_ERR_INVALID_ARGUMENT, "null col_idx");
         for (int32_t p = a; p < b; ++p) {
             const int32_t j = col_idx[p];

@@ -259,11 +259,13 @@ bsa_status bsa_norm_rope_select(const void* xq, const void* xk, const void* wq, 
                                 int32_t* row_ptr, int32_t* col_idx, void* workspace,
                                 size_t workspace_bytes, void* hip_stream);
 
-/* Host-side validator for a CSR held in host memory: row_ptr[0] == 0, non-decreasing,
- * every row's indices strictly ascending in [0, n_blocks). Returns BSA_OK or
+/* Host-side validator for a CSR held in host memory: row_ptr_host holds row_ptr_len entries and
+ * col_idx_host col_idx_len entries (the caller's buffer sizes; nothing past them is read).
+ * Checks row_ptr_len == rows + 1, row_ptr[0] == 0, non-decreasing, row_ptr[rows] <= col_idx_len,
+ * and every row's indices strictly ascending in [0, n_blocks). Returns BSA_OK or
  * BSA_ERR_INVALID_ARGUMENT with the first violation in bsa_last_error(). */
-bsa_status bsa_check_csr(const int32_t* row_ptr_host, const int32_t* col_idx_host, int32_t rows,
-                         int32_t n_blocks);
+bsa_status bsa_check_csr(const int32_t* row_ptr_host, int64_t row_ptr_len, const int32_t* col_idx_host,
+                         int64_t col_idx_len, int32_t rows, int32_t n_blocks);
 
 /* Static name of a status code. */
 const char* bsa_status_string(bsa_status status);

@@ -237,8 +237,11 @@ def test_no_device_status_without_gpu():
 
 def test_check_csr():
     bsa.bsa_check_csr(np.array([0, 2, 3]), np.array([0, 3, 1]), 2, 4)
+    bsa.bsa_check_csr(np.array([0, 2, 3]), np.array([0, 3, 1, 99]), 2, 4)  # spare entries are not read
     for rp, ci in [([0, 2, 3], [1, 0, 0]), ([0, 2, 3], [0, 4, 1]), ([1, 2, 3], [0, 1, 2]), ([0, 2, 1], [0, 1]),
-                   ([0, 1, 2], [0, -1])]:
+                   ([0, 1, 2], [0, -1]),
+                   ([0, 2, 3], [0, 3]),  # row 1 ends past col_idx (checked in C, from the length passed)
+                   ([0, 2], [0, 1]), ([0, 1, 2, 3], [0, 1, 2])]:  # row_ptr not rows + 1 long
         with pytest.raises(bsa.BsaError) as e:
             bsa.bsa_check_csr(np.array(rp), np.array(ci), 2, 4)
         assert e.value.status == 1
