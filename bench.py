@@ -38,9 +38,9 @@ def kept_flops(row_ptr, col_idx, S, block):
     n = (S + block - 1) // block
     sizes = np.full(n, block, dtype=np.int64)
     sizes[-1] = S - (n - 1) * block
-    rp = row_ptr.astype(np.int64)
-    keys = np.add.reduceat(sizes[col_idx.astype(np.int64)], rp[:-1]) if col_idx.size else np.zeros(rp.size - 1)
-    keys = np.where(np.diff(rp) > 0, keys, 0)
+    rp = np.asarray(row_ptr, np.int64)
+    csum = np.concatenate([[0], np.cumsum(sizes[np.asarray(col_idx, np.int64)[:rp[-1]]])])
+    keys = csum[rp[1:]] - csum[rp[:-1]]  # keys kept by each row (empty rows included)
     qsz = np.tile(sizes, (rp.size - 1) // n)
     return int(np.sum(qsz * keys))
 
@@ -408,6 +408,17 @@ def stats(ms):
             "min": round(float(np.min(ms)), 4)}
 
 
+def workload_name(config, heads, seed, B, H, S, D, block, keep_ratio, kept, n):
+    """The bench line's config.workload string."""
+    name = config
+    if heads:
+        name += " (first %d heads: one rank's share)" % H
+    if seed is not None:
+        name += " (seed %d)" % seed
+    return "%s: B=%d H=%d S=%d D=%d block=%d keep_ratio=%g (%d of %d key blocks kept)" % (
+        name, B, H, S, D, block, keep_ratio, kept, n)
+
+
 def head_slice(q, k, v, heads):
     """The first `heads` heads of each tensor: one rank's share when heads are sharded."""
     if not heads:
@@ -515,6 +526,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="720p", choices=["480p", "720p", "long"])
+    ap.add_argument("--seed", type=int, default=None,
+                    help="draw the workload from this seed instead of its own (same shapes and recipe)")
     ap.add_argument("--heads", type=int, default=0,
                     help="run only the first HEADS heads of the workload: one rank's share when the "
                          "heads are sharded across GPUs (5 of 40 on eight GPUs)")
@@ -570,7 +583,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    q, k, v, cfg = gen.make_config(args.config)
+    q, k, v, cfg = gen.make_config(args.config, seed=args.seed)
     q, k, v = head_slice(q, k, v, args.heads)
     B, H, S, D = q.shape
     block, r = cfg["block"], cfg["keep_ratio"]
@@ -702,9 +715,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded noise + smooth (t,h,w) locality term, bf16)",
-        "config": {"workload": "%s%s: B=%d H=%d S=%d D=%d block=%d keep_ratio=%g (%d of %d key blocks kept)"
-                               % (args.config, " (first %d heads: one rank's share)" % H if args.heads else "",
-                                  B, H, S, D, block, r, kept, n),
+        "config": {"workload": workload_name(args.config, args.heads, args.seed, B, H, S, D, block, r, kept, n),
                    "global_batch": B, "seq_len": S, "heads": H, "head_dim": D, "block": block,
                    "keep_ratio": r, "parallelism": "single GPU"},
         "attention_ms": round(fwd_ms, 4),
@@ -721,7 +732,9 @@ def main():
         "select_hbm_gbs": round(pool_bytes / (sel_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_from_profile(kernel_sha) if not args.heads else None,
+                     # the committed counters cover the whole default 720p call only
+                     "traffic": (traffic_from_profile(kernel_sha)
+                                 if not args.heads and args.config == "720p" and args.seed is None else None),
                      "kernel": "attn_kernel<128,128,bf16>",
                      "measured_peak": peak["bf16_tflops"],
                      "frac_measured_peak": round(fwd_tflops / peak["bf16_tflops"], 4)},

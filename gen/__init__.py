@@ -103,9 +103,11 @@ def make_qkv(B: int, H: int, S: int, D: int, seed: int, grid=None, alpha: float 
     return tuple(out)
 
 
-def make_config(name: str):
-    """(q, k, v, cfg) for one of CONFIGS."""
+def make_config(name: str, seed=None):
+    """(q, k, v, cfg) for one of CONFIGS, optionally with another seed."""
     cfg = dict(CONFIGS[name])
+    if seed is not None:
+        cfg["seed"] = int(seed)
     q, k, v = make_qkv(cfg["B"], cfg["H"], cfg["S"], cfg["D"], cfg["seed"], cfg["grid"], cfg["alpha"])
     return q, k, v, cfg
 

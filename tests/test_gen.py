@@ -37,3 +37,14 @@ def test_smooth_term_has_unit_scale_and_period():
     np.testing.assert_allclose(np.sum(phi ** 2, axis=1), 3.0, atol=1e-12)
     # one period per axis: token (t=0,h=0,w=0) equals the wrap-around point
     np.testing.assert_allclose(phi[0], gen.smooth_features((4, 5, 6), 120)[0])
+
+
+def test_config_seed_override():
+    q, k, v, cfg = gen.make_config("tiny")
+    q7, k7, v7, cfg7 = gen.make_config("tiny", seed=7)
+    assert cfg7["seed"] == 7 and cfg["seed"] == gen.CONFIGS["tiny"]["seed"]
+    assert gen.CONFIGS["tiny"]["seed"] != 7  # the table itself is left alone
+    assert not np.array_equal(q, q7)
+    ref = gen.make_qkv(cfg7["B"], cfg7["H"], cfg7["S"], cfg7["D"], 7, cfg7["grid"], cfg7["alpha"])
+    for x, y in zip((q7, k7, v7), ref):
+        assert np.array_equal(x, y)
