@@ -84,7 +84,7 @@ int32_t bsa_num_kept(int32_t n_blocks, double keep_ratio);
  * 2 * B*H*n*D * 4, rounded up to 256. 0 on invalid shape. Host only. */
 size_t bsa_select_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t block);
 
-/* Block means ([KC] 动态稀疏量化注意力: "块级均值"): xbar[b,h,i,:] = the mean of x over
+/* Block means ([KC] 动态稀疏量化注意力, importance estimated from block-level means): xbar[b,h,i,:] = the mean of x over
  * the valid tokens of block i, accumulated in fp32. x: bf16 [B,H,S,D] (device).
  * xbar: fp32 [B,H,n,D] (device, caller-allocated). Exposed for parity checks; bsa_select
  * computes the same means internally. */

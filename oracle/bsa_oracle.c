@@ -127,7 +127,7 @@ int32_t oracle_num_kept(int32_t n, double keep_ratio) {
     return (int32_t)k;
 }
 
-/* ---- step 1: block means of Q or K ([KC] 动态稀疏量化注意力: "块级均值") ------------ */
+/* ---- step 1: block means of Q or K ([KC] 动态稀疏量化注意力: importance from block-level means) */
 
 void oracle_pool(const uint16_t* x, int32_t B, int32_t H, int32_t S, int32_t D, int32_t block,
                  double* xbar /* [B*H, n, D] */) {
