@@ -25,8 +25,8 @@ MUTANTS = [
      "T->scale[bh * T->nblk]", 0),
     ("fp8 block scale: head offset missing", "T->scale[bh * T->nblk + t / T->block]", "T->scale[t / T->block]", 0),
     ("fp8 block scale dropped", ": (double)T->scale[bh * T->nblk + t / T->block];", ": 1.0;", 0),
-    ("fp8 dequantisation divides by the scale", "return oracle_e4m3_value(T->e4m3[off]) * sc;",
-     "return oracle_e4m3_value(T->e4m3[off]) / sc;", 0),
+    ("fp8 dequantisation divides by the scale", "return e4m3_table[T->e4m3[off]] * sc;",
+     "return e4m3_table[T->e4m3[off]] / sc;", 0),
     ("V channel scale: the first channel's", "T->chan_scale[bh * T->D + d]", "T->chan_scale[bh * T->D]", 0),
     ("V channel scale: head offset missing", "T->chan_scale[bh * T->D + d]", "T->chan_scale[d]", 0),
     ("fp8-QK: K dequantised with Q's scales", "K = {NULL, k8, k_scale, NULL,", "K = {NULL, k8, q_scale, NULL,", 0),
