@@ -70,6 +70,7 @@ def cpu_baseline(q, k, v, cfg, budget_tokens):
     t0 = time.perf_counter()
     ref = oracle.select(q, k, cfg["block"], cfg["keep_ratio"])
     t_sel = time.perf_counter() - t0
+    budget_tokens = min(budget_tokens, B * H * S)
     tok = np.random.default_rng(0).choice(B * H * S, size=budget_tokens, replace=False)
     t0 = time.perf_counter()
     oracle.attention(q, k, v, cfg["block"], ref["row_ptr"], ref["col_idx"], tokens=tok)
@@ -525,7 +526,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="720p", choices=["480p", "720p", "long"])
+    ap.add_argument("--config", default="720p", choices=["tiny", "480p", "720p", "long"])
     ap.add_argument("--seed", type=int, default=None,
                     help="draw the workload from this seed instead of its own (same shapes and recipe)")
     ap.add_argument("--heads", type=int, default=0,
@@ -735,7 +736,7 @@ def main():
                      # the committed counters cover the whole default 720p call only
                      "traffic": (traffic_from_profile(kernel_sha)
                                  if not args.heads and args.config == "720p" and args.seed is None else None),
-                     "kernel": "attn_kernel<128,128,bf16>",
+                     "kernel": "attn_kernel<%d,%d,bf16>" % (D, block),
                      "measured_peak": peak["bf16_tflops"],
                      "frac_measured_peak": round(fwd_tflops / peak["bf16_tflops"], 4)},
         "mfma_peak_measured": peak,

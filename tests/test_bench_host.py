@@ -43,3 +43,10 @@ def test_help_lists_the_modes():
     assert r.returncode == 0
     for opt in ("--all-configs", "--heads", "--mfma-peak", "--seed", "--sweep"):
         assert opt in r.stdout
+
+
+def test_cpu_baseline_on_a_workload_smaller_than_the_sample():
+    import gen
+    q, k, v, cfg = gen.make_config("tiny")
+    r = bench.cpu_baseline(q, k, v, cfg, 8192)
+    assert r["kind"] == "oracle" and r["value"] > 0 and "2048 of 2048" in r["sample"]
