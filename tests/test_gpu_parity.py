@@ -419,6 +419,26 @@ def test_select_long_rows(S, block, r):
     check_lists(rp.cpu().numpy(), ci.cpu().numpy(), ref)
 
 
+def test_select_and_forward_at_the_largest_supported_sequence():
+    """bsa_select at its limit of 8192 blocks per sequence (S = 8192 * 64 - 7, the last block
+    partial): every list against the oracle, and the forward on those lists on sampled rows
+    (the first and last block included)."""
+    B, H, D, block, r = 1, 1, 64, 64, 0.01
+    S = 8192 * 64 - 7
+    q, k, v = gen.make_qkv(B, H, S, D, 91, grid=(S, 1, 1), alpha=1.0)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    rp, ci = bsa.bsa_select(qd, kd, block, r)
+    ref = oracle.select(q, k, block, r)
+    assert oracle.num_blocks(S, block) == 8192
+    check_lists(rp.cpu().numpy(), ci.cpu().numpy(), ref)
+    out = bsa.bsa_forward(qd, kd, vd, block, rp, ci)
+    tok = np.unique(np.concatenate([np.random.default_rng(5).integers(0, S, 512), [0, 63, 64, S - 57, S - 1]]))
+    got = to_f64(out.reshape(-1, D)[torch.from_numpy(tok).cuda()])
+    expect = oracle.attention(q, k, v, block, rp.cpu().numpy(), ci.cpu().numpy(), tokens=tok)
+    mx, mean = errors(got, expect)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (mx, mean)
+
+
 @pytest.mark.parametrize("i", [165, 169, 178, 10])
 def test_large_magnitude_inputs_bf16_bar_scales_with_output(i):
     """Inputs with a strong smooth term (|x| up to about 10, outputs of about 1.6 on average):
