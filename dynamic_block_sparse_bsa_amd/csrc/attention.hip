@@ -27,7 +27,9 @@
 //
 // LDS layout: K and V tiles are row-major [64 keys][D], 16-byte chunks XOR-swizzled per row
 // so that both the K-operand reads (16 rows, one chunk) and the transposing V reads
-// (4 rows, 4 chunks) hit distinct banks.
+// (4 rows, 4 chunks) hit distinct banks. The full fp8 mode runs three waves per SIMD: its
+// registers then cannot hold Q, so each wave keeps its 32 E4M3 Q rows in LDS after the stages,
+// in the K tile's layout, and reads them back before each sub-tile's S^T MFMAs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -74,10 +76,11 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// max / sum of a value over lanes l and l^32 (v_permlane32_swap: no LDS round trip).
+// max / sum of a value over lanes l and l^32 (v_permlane32_swap: no LDS round trip). Maxima use
+// the IEEE maximum, which compiles to v_maximum3_f32 without the NaN-quieting moves of fmaxf.
 __device__ __forceinline__ float pair_max(float x) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -114,10 +117,16 @@ struct Cfg {
     // Direct global->LDS loads move 1 KiB per wave instruction ("segment").
     static constexpr int KRPS = 1024 / KROWB, VRPS = 1024 / VROWB;  // rows per segment
     static constexpr int KSEGW = KTILE / 1024 / NW, VSEGW = VTILE / 1024 / NW;  // per wave
-    // Waves per SIMD that LDS allows (160 KiB per CU, four SIMDs), at most two: one for
-    // 128-dim 64-token blocks (64 KiB per two-wave workgroup), so those may use 512 registers.
+    // Waves per SIMD that LDS allows (160 KiB per CU, four SIMDs), at most two (three for the
+    // full fp8 mode, below): one for 128-dim 64-token blocks (64 KiB per two-wave workgroup), so
+    // those may use 512 registers.
     static constexpr int LDS_WAVES = (160 * 1024 / (2 * STAGE)) * NW / 4;
-    static constexpr int WAVES_PER_SIMD = LDS_WAVES >= 2 ? 2 : 1;
+    // Full fp8 mode: three waves per SIMD where LDS allows them with the E4M3 Q rows moved from
+    // registers into LDS (which the register budget of three waves needs).
+    static constexpr int QROWS_BYTES = NW * 32 * D;
+    static constexpr bool QINLDS = PV8 && (160 * 1024 / (2 * STAGE + QROWS_BYTES)) * NW / 4 >= 3;
+    static constexpr int QLDS = QINLDS ? QROWS_BYTES : 0;
+    static constexpr int WAVES_PER_SIMD = QINLDS ? 3 : (LDS_WAVES >= 2 ? 2 : 1);
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -136,12 +145,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 template <int D, int BLK, int MODE>
-__global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(Cfg<D, BLK, MODE>::WAVES_PER_SIMD, 2)))
+__global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(Cfg<D, BLK, MODE>::WAVES_PER_SIMD, Cfg<D, BLK, MODE>::WAVES_PER_SIMD > 2 ? Cfg<D, BLK, MODE>::WAVES_PER_SIMD : 2)))
 attn_kernel(const AttnArgs a) {
     using C = Cfg<D, BLK, MODE>;
     constexpr bool FP8 = C::FP8, PV8 = C::PV8;
     static_assert(C::KSEGW >= 1 && C::VSEGW >= 1, "tile too small for the workgroup");
-    __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds[2 * C::STAGE + C::QLDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -282,6 +291,17 @@ attn_kernel(const AttnArgs a) {
         const int c = FP8 ? (4 * (st >> 1) + 2 * h + (st & 1)) : (2 * st + h);
         k_rd[st] = l32 * C::KROWB + 16 * swz<C::KCH>(l32, c);
     }
+    // Full fp8 mode: the wave's 32 E4M3 Q rows go to LDS (in the K tile's swizzled layout, so
+    // the K read offsets serve), and are read back before each sub-tile's S^T MFMAs.
+    char* const qlds = lds + 2 * C::STAGE + wave * 32 * D;
+    if constexpr (C::QINLDS) {
+#pragma unroll
+        for (int st = 0; st < C::QSTEPS; ++st) {
+            const i32x8 v = qf[st];
+            *(i32x4*)(qlds + k_rd[2 * st]) = (i32x4){v[0], v[1], v[2], v[3]};
+            *(i32x4*)(qlds + k_rd[2 * st + 1]) = (i32x4){v[4], v[5], v[6], v[7]};
+        }
+    }
     const int gi = lane & 15;
     uint32_t v_rd1[D / 32], v_rd2[D / 32];
     if constexpr (PV8) {
@@ -315,10 +335,20 @@ attn_kernel(const AttnArgs a) {
     // 0..31 accumulates sum_k P8[k][query].
     f32x16 lacc = (f32x16){};
     const int one_bits = (PV8 && l32 == 0) ? 0x38383838 : 0;  // E4M3 1.0 = 0x38
-    const i32x8 ones = {one_bits, one_bits, one_bits, one_bits, one_bits, one_bits, one_bits, one_bits};
 
-    auto compute = [&](const char* kt, int nkeys, float tscale) __attribute__((always_inline)) {
+    auto compute = [&](const char* kt, int nkeys, float tscale, const char* qsrc) __attribute__((always_inline)) {
         const char* vt = kt + C::KTILE;
+        frag_t qv[C::QSTEPS];
+#pragma unroll
+        for (int st = 0; st < C::QSTEPS; ++st) {
+            if constexpr (C::QINLDS) {
+                u32x4 lo = *(const u32x4*)(qsrc + k_rd[2 * st]);
+                u32x4 hi = *(const u32x4*)(qsrc + k_rd[2 * st + 1]);
+                qv[st] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            } else {
+                qv[st] = qf[st];
+            }
+        }
         // S^T = K Q^T for the 64 keys (two 32-key halves); A fragments read in a batch.
         f32x16 s[2];
 #pragma unroll
@@ -339,8 +369,8 @@ attn_kernel(const AttnArgs a) {
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int st = 0; st < C::QSTEPS; ++st) {
-                if constexpr (FP8) s[kh] = mfma_fp8(kf[st], qf[st], s[kh]);
-                else s[kh] = mfma_bf16(kf[st], qf[st], s[kh]);
+                if constexpr (FP8) s[kh] = mfma_fp8(kf[st], qv[st], s[kh]);
+                else s[kh] = mfma_bf16(kf[st], qv[st], s[kh]);
             }
             __builtin_amdgcn_s_setprio(0);
         }
@@ -364,7 +394,7 @@ attn_kernel(const AttnArgs a) {
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kh][e]);
+                for (int e = 0; e < 16; ++e) mx = __builtin_elementwise_maximum(mx, s[kh][e]);  // v_maximum3_f32
             mx = pair_max(mx);
             const float mt = mx * tscale;
             if (__any(mt > m_used)) {
@@ -387,7 +417,10 @@ attn_kernel(const AttnArgs a) {
                                                     fast_exp2(__builtin_fmaf(s[kh][v + 3], tscale, off)), w, true);
                 p8[wd] = w;
             }
-            lacc = mfma_fp8(ones, p8, lacc);
+            int ob = one_bits;  // rebuilt per sub-tile: cheaper than keeping 8 registers live
+            asm volatile("" : "+v"(ob));
+            const i32x8 ones_v = {ob, ob, ob, ob, ob, ob, ob, ob};
+            lacc = mfma_fp8(ones_v, p8, lacc);
 #pragma unroll
             for (int ds = 0; ds < D / 32; ++ds) {
                 const u32x4 lo = *(const u32x4*)(vt + v_rd1[ds]);
@@ -504,9 +537,9 @@ attn_kernel(const AttnArgs a) {
     // without them the wait-count analysis assumes the reads may see the in-flight writes
     // and waits for every load before the first read, which would serialise the pipeline.
     auto step = [&](const char* __restrict__ cur, char* __restrict__ nxt, int nkeys, float tsc,
-                    int load_key0, int load_nk) __attribute__((always_inline)) {
+                    int load_key0, int load_nk, const char* __restrict__ qsrc) __attribute__((always_inline)) {
         if (load_nk > 0) issue_tile(load_key0, load_nk, nxt);
-        if (nkeys > 0) compute(cur, nkeys, tsc);
+        if (nkeys > 0) compute(cur, nkeys, tsc, qsrc);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
     };
@@ -515,9 +548,9 @@ attn_kernel(const AttnArgs a) {
             const int key0 = j * BLK;
             const int nk0 = keys_at(key0), nk1 = keys_at(key0 + KT);
             const float tsb = ts;
-            step(lds, lds + C::STAGE, nk0, tsb, key0 + KT, nk1);
+            step(lds, lds + C::STAGE, nk0, tsb, key0 + KT, nk1, qlds);
             next_block();
-            step(lds + C::STAGE, lds, nk1, tsb, j * BLK, j >= 0 ? keys_at(j * BLK) : 0);
+            step(lds + C::STAGE, lds, nk1, tsb, j * BLK, j >= 0 ? keys_at(j * BLK) : 0, qlds);
         }
     } else {
         static_assert(BLK == KT, "blocks of one or two sub-tiles");
@@ -525,12 +558,12 @@ attn_kernel(const AttnArgs a) {
             int nk = keys_at(j * BLK);
             float tsb = ts;
             next_block();
-            step(lds, lds + C::STAGE, nk, tsb, j * BLK, j >= 0 ? keys_at(j * BLK) : 0);
+            step(lds, lds + C::STAGE, nk, tsb, j * BLK, j >= 0 ? keys_at(j * BLK) : 0, qlds);
             if (j < 0) break;
             nk = keys_at(j * BLK);
             tsb = ts;
             next_block();
-            step(lds + C::STAGE, lds, nk, tsb, j * BLK, j >= 0 ? keys_at(j * BLK) : 0);
+            step(lds + C::STAGE, lds, nk, tsb, j * BLK, j >= 0 ? keys_at(j * BLK) : 0, qlds);
         }
     }
 
